@@ -1,0 +1,169 @@
+"""SharQ linear hot path for AMD MI355X (gfx950).
+
+Thin PyTorch-facing wrappers over the C ABI in ``include/sharq.h``: they check
+tensor dtypes/devices, allocate outputs with ``torch.empty`` and pass raw device
+pointers and the current HIP stream. All arithmetic runs in libsharq.so.
+
+    prep = prepare(x, gamma=None, n=2, m=4)        # x: bf16 [T, K] on the GPU
+    wq = quantize_mxfp4(w)                         # w: bf16 [O, K]
+    y = linear(prep, wq)                           # fp32 [T, O]
+"""
+
+from __future__ import annotations
+
+from typing import NamedTuple, Optional
+
+from . import _lib
+from ._lib import SharqError, status_string  # noqa: F401
+
+__all__ = [
+    "Prepared",
+    "MXFP4",
+    "prepare",
+    "quantize_mxfp4",
+    "linear",
+    "linear_grouped",
+    "silu_mul",
+    "SharqError",
+    "status_string",
+]
+
+
+class Prepared(NamedTuple):
+    """Outputs of the prepare operator (all uint8 device tensors)."""
+    bb_codes: "object"    # [T, K/2]
+    bb_scales: "object"   # [T, K/32]
+    res_codes: "object"   # [T, K/2]
+    res_scales: "object"  # [T, K/32]
+    mask: "object"        # [T, K/8] or None
+
+
+class MXFP4(NamedTuple):
+    codes: "object"   # uint8 [..., K/2]
+    scales: "object"  # uint8 [..., K/32]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: Optional[Prepared] = None) -> Prepared:
+    """Fused prepare: N:M mask, MXFP4 backbone, residual against it, MXFP4 residual."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x", 2)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous along K")
+    T, K = x.shape
+    if gamma is not None:
+        _need(gamma, torch.bfloat16, "gamma", 1)
+        gamma = gamma.contiguous()
+    if out is None:
+        kw = dict(dtype=torch.uint8, device=x.device)
+        out = Prepared(torch.empty((T, K // 2), **kw), torch.empty((T, K // 32), **kw),
+                       torch.empty((T, K // 2), **kw), torch.empty((T, K // 32), **kw),
+                       torch.empty((T, K // 8), **kw) if with_mask else None)
+    st = _lib.call("sharq_prepare", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), n, m,
+                   out.bb_codes.data_ptr(), out.bb_scales.data_ptr(), out.res_codes.data_ptr(),
+                   out.res_scales.data_ptr(), _ptr(out.mask), _stream(x.device))
+    _lib.check("sharq_prepare", st)
+    return out
+
+
+def quantize_mxfp4(x, out: Optional[MXFP4] = None) -> MXFP4:
+    """Plain MXFP4 along the last axis of a bf16 [R, K] tensor (e.g. a weight [O, K])."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x", 2)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous along K")
+    R, K = x.shape
+    if out is None:
+        out = MXFP4(torch.empty((R, K // 2), dtype=torch.uint8, device=x.device),
+                    torch.empty((R, K // 32), dtype=torch.uint8, device=x.device))
+    st = _lib.call("sharq_quantize_mxfp4", x.data_ptr(), R, K, x.stride(0), out.codes.data_ptr(),
+                   out.scales.data_ptr(), _stream(x.device))
+    _lib.check("sharq_quantize_mxfp4", st)
+    return out
+
+
+def linear(prep: Prepared, w: MXFP4, out=None):
+    """Two-path FP4 GEMM: Y = deq(backbone) W^T + deq(residual) W^T, fp32 [T, O]."""
+    torch = _torch()
+    for name in ("bb_codes", "bb_scales", "res_codes", "res_scales"):
+        _need(getattr(prep, name), torch.uint8, name, 2)
+    _need(w.codes, torch.uint8, "w.codes", 2)
+    _need(w.scales, torch.uint8, "w.scales", 2)
+    T, Kh = prep.bb_codes.shape
+    O = w.codes.shape[0]
+    K = 2 * Kh
+    if w.codes.shape[1] != Kh:
+        raise ValueError("weight K does not match the activation K")
+    if out is None:
+        out = torch.empty((T, O), dtype=torch.float32, device=prep.bb_codes.device)
+    _need(out, torch.float32, "out", 2)
+    st = _lib.call("sharq_linear", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(), prep.res_codes.data_ptr(),
+                   prep.res_scales.data_ptr(), w.codes.data_ptr(), w.scales.data_ptr(), T, O, K,
+                   out.data_ptr(), out.stride(0), _stream(out.device))
+    _lib.check("sharq_linear", st)
+    return out
+
+
+def linear_grouped(prep: Prepared, w: MXFP4, seg_offsets, a_rows=None, out=None):
+    """Grouped two-path GEMM over expert segments. w.codes is [E, O, K/2];
+    seg_offsets int32 [E+1]; a_rows int32 [P] (source row of each sorted pair) or None."""
+    torch = _torch()
+    _need(w.codes, torch.uint8, "w.codes", 3)
+    _need(w.scales, torch.uint8, "w.scales", 3)
+    _need(seg_offsets, torch.int32, "seg_offsets", 1)
+    E, O, Kh = w.codes.shape
+    K = 2 * Kh
+    if seg_offsets.numel() != E + 1:
+        raise ValueError("seg_offsets must have E + 1 entries")
+    if a_rows is not None:
+        _need(a_rows, torch.int32, "a_rows", 1)
+        P = a_rows.numel()
+    else:
+        P = prep.bb_codes.shape[0]
+    if out is None:
+        out = torch.empty((P, O), dtype=torch.float32, device=w.codes.device)
+    st = _lib.call("sharq_linear_grouped", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
+                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), _ptr(a_rows), seg_offsets.data_ptr(), E,
+                   w.codes.data_ptr(), w.scales.data_ptr(), P, O, K, out.data_ptr(), _stream(out.device))
+    _lib.check("sharq_linear_grouped", st)
+    return out
+
+
+def silu_mul(gu, out=None):
+    """h = bf16(silu(gu[:, :I]) * gu[:, I:]) for a fused gate|up output gu fp32 [T, 2I]."""
+    torch = _torch()
+    _need(gu, torch.float32, "gu", 2)
+    if not gu.is_contiguous():
+        raise ValueError("gu must be contiguous")
+    T, I2 = gu.shape
+    I = I2 // 2
+    if out is None:
+        out = torch.empty((T, I), dtype=torch.bfloat16, device=gu.device)
+    st = _lib.call("sharq_silu_mul", gu.data_ptr(), T, I, out.data_ptr(), _stream(gu.device))
+    _lib.check("sharq_silu_mul", st)
+    return out

@@ -1,0 +1,73 @@
+"""ctypes view of libsharq.so (the C ABI declared in include/sharq.h).
+
+Only argument marshalling lives here. Every step of the hot path runs in the
+HIP library; if the library cannot be loaded, loading fails loudly.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsharq.so")
+
+SHARQ_OK = 0
+SHARQ_EINVAL = -1
+SHARQ_EALIGN = -2
+SHARQ_EUNSUPPORTED = -3
+SHARQ_EHIP = -4
+SHARQ_ENOTIMPL = -5
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+
+# name -> (restype, argtypes); mirrors include/sharq.h
+SIGNATURES = {
+    "sharq_status_string": (ctypes.c_char_p, [_INT]),
+    "sharq_abi_version": (_INT, []),
+    "sharq_prepare": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _INT, _P, _P, _P, _P, _P, _P]),
+    "sharq_quantize_mxfp4": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "sharq_linear": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    "sharq_linear_grouped": (_INT, [_P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "sharq_silu_mul": (_INT, [_P, _I64, _I64, _P, _P]),
+}
+
+_lib = None
+
+
+class SharqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsharq.so once. Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m activation_sparsity_fp4_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sharq_status_string(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != SHARQ_OK:
+        raise SharqError(fn, status)
+
+
+def call(name: str, *args) -> int:
+    """Call an ABI entry point with raw integers (device addresses) and return its status."""
+    return getattr(lib(), name)(*args)

@@ -1,0 +1,60 @@
+// SiLU-gated product between a fused gate|up projection and the down
+// projection (glue around the SharQ linears, not part of the method):
+// h[t][i] = bf16_rne(silu(g) * u), g = gu[t][i], u = gu[t][I + i].
+// HBM-bound elementwise kernel: each lane reads 8 gate and 8 up floats
+// (2 x 32 B) and writes 8 bf16 (16 B).
+
+#include "sharq_device.h"
+#include "sharq_internal.h"
+
+namespace sharq {
+namespace {
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// silu(g) * u without overflow: with h = exp(-|g| / 2) (in (0, 1]),
+//   g >= 0: g * u / (1 + h^2)           (h^2 = exp(-g))
+//   g <  0: ((g * u) * h) * h / (1 + h^2)  (= g u e^g / (1 + e^g))
+// The negative branch multiplies by the two half-exponentials one at a time so
+// results down to the fp32 normal range survive even when e^g alone is subnormal.
+__device__ __forceinline__ float silu_times(float g, float u) {
+  const float h = __expf(-0.5f * fabsf(g));
+  const float den = 1.0f + h * h;
+  const float gu = g * u;
+  return g >= 0.0f ? gu / den : ((gu * h) * h) / den;
+}
+
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ gu, int64_t I, uint32_t groups_per_row,
+                                                       uint32_t total, uint16_t* __restrict__ h) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const uint32_t t = gid / groups_per_row;
+  const uint32_t c = gid - t * groups_per_row;
+  const float4* g = reinterpret_cast<const float4*>(gu + (int64_t)t * 2 * I + 8 * (int64_t)c);
+  const float4* u = reinterpret_cast<const float4*>(gu + (int64_t)t * 2 * I + I + 8 * (int64_t)c);
+  const float4 g0 = g[0], g1 = g[1], u0 = u[0], u1 = u[1];
+  const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = silu_times(gv[2 * k], uv[2 * k]);
+    const float b = silu_times(gv[2 * k + 1], uv[2 * k + 1]);
+    out[k] = bf16_rne_bits(a) | (bf16_rne_bits(b) << 16);
+  }
+  reinterpret_cast<uint4*>(h + (int64_t)t * I)[c] = make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+}  // namespace
+
+hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {
+  const uint32_t gpr = (uint32_t)(I / 8);
+  const uint32_t total = (uint32_t)(T * gpr);
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, gu, I, gpr, total, h);
+  return hipGetLastError();
+}
+
+}  // namespace sharq

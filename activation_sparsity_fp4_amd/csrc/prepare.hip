@@ -1,0 +1,249 @@
+// Fused SharQ prepare kernel for gfx950.
+//
+// What it computes (page "SharQ: Bridging Activation Sparsity and FP4
+// Quantization for LLM Inference", Abstract and Section 1): per activation row,
+// an online N:M mask keeps the N largest |x'| of every M entries along K
+// (x' = x * gamma when the RMSNorm weight is absorbed); the kept entries form a
+// sparse backbone coded in MXFP4; the residual x' - dequant(backbone) is coded
+// in MXFP4 with its own scales.
+//
+// Work decomposition: one lane owns one 32-entry MX block of one row, so every
+// block reduction (amax, scale) and every N:M group (4 or 16 entries, both
+// dividing 32) stays inside the lane's registers and no cross-lane traffic is
+// needed. A lane reads 64 contiguous bytes of bf16 (four 16-byte loads) and
+// writes 16 + 16 bytes of codes, two scale bytes and a 32-bit mask word; lanes
+// of a wave own consecutive blocks of a row, so all accesses are contiguous
+// across the wave. The kernel is HBM-bound: 2 bytes read and 1.1875 bytes
+// written per element.
+//
+// Selection: magnitudes are compared as integer bit patterns. When the low
+// bits of every |x'| in a block are zero (always for bf16 inputs; for x * gamma
+// unless the product is an fp32 subnormal) the group position is folded into
+// those low bits, which makes every key unique and orders equal magnitudes by
+// lower index. Top-2 of 4 is then a max/min tournament and top-8 of 16 uses two
+// 8-key sorting networks and a bitonic half-cleaner. Blocks with non-zero low
+// bits take an exact pairwise-rank path instead.
+//
+// Quantisation uses the gfx950 scaled converters (v_cvt_scalef32_pk_fp4_f32,
+// v_cvt_scalef32_pk_f32_fp4), whose rounding (nearest-even, saturation at 6,
+// sign kept on zero) matches the MXFP4 rule exactly for every finite input.
+
+#include "sharq_device.h"
+#include "sort_network.h"
+#include "sharq_internal.h"
+
+namespace sharq {
+
+// Mask bits (one per entry, bit k) of the kept entries of a block for n:m.
+template <int N, int M>
+__device__ __forceinline__ uint32_t select_fast(const float (&x)[32]) {
+  static_assert((N == 2 && M == 4) || (N == 8 && M == 16), "pattern");
+  uint32_t mask = 0;
+  if constexpr (M == 4) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      uint32_t k[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        k[i] = (__float_as_uint(x[4 * g + i]) & 0x7FFFFFFCu) | (3u - i);
+      const uint32_t a = max(k[0], k[1]), b = min(k[0], k[1]);
+      const uint32_t c = max(k[2], k[3]), d = min(k[2], k[3]);
+      const uint32_t second = max(max(min(a, c), b), d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mask |= (k[i] >= second ? 1u : 0u) << (4 * g + i);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      uint32_t k[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        k[i] = (__float_as_uint(x[16 * g + i]) & 0x7FFFFFF0u) | (15u - i);
+      uint32_t lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { lo[i] = k[i]; hi[i] = k[8 + i]; }
+#pragma unroll
+      for (int c = 0; c < kSort8Size; ++c) {
+        const int i = kSort8[c][0], j = kSort8[c][1];
+        const uint32_t p = max(lo[i], lo[j]), q = min(lo[i], lo[j]);
+        lo[i] = p; lo[j] = q;
+        const uint32_t r = max(hi[i], hi[j]), s = min(hi[i], hi[j]);
+        hi[i] = r; hi[j] = s;
+      }
+      uint32_t thr = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) thr = min(thr, max(lo[i], hi[7 - i]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mask |= (k[i] >= thr ? 1u : 0u) << (16 * g + i);
+    }
+  }
+  return mask;
+}
+
+// Exact selection for any block: entry i is kept when fewer than N entries of
+// its group beat it (larger |x'|, or equal |x'| at a lower index).
+template <int N, int M>
+__device__ __forceinline__ uint32_t select_exact(const float (&x)[32]) {
+  uint32_t mask = 0;
+#pragma unroll
+  for (int g = 0; g < 32 / M; ++g) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const uint32_t ai = __float_as_uint(x[M * g + i]) & 0x7FFFFFFFu;
+      int beaten = 0;
+#pragma unroll
+      for (int j = 0; j < M; ++j) {
+        if (j == i) continue;
+        const uint32_t aj = __float_as_uint(x[M * g + j]) & 0x7FFFFFFFu;
+        beaten += (aj > ai || (aj == ai && j < i)) ? 1 : 0;
+      }
+      mask |= (beaten < N ? 1u : 0u) << (M * g + i);
+    }
+  }
+  return mask;
+}
+
+template <int N, int M, bool kGamma>
+__global__ __launch_bounds__(256) void prepare_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma,
+    uint32_t blocks_per_row, uint32_t total_blocks,
+    uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_scales,
+    uint8_t* __restrict__ res_codes, uint8_t* __restrict__ res_scales,
+    uint8_t* __restrict__ mask_out) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_blocks) return;
+  const uint32_t t = gid / blocks_per_row;
+  const uint32_t b = gid - t * blocks_per_row;
+
+  // load 32 bf16 (64 B) and widen to fp32
+  const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * ldx + (int64_t)b * kBlock);
+  uint4 raw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = src[i];
+  float xv[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xv[8 * i + 2 * j] = bf16_lo(w[j]);
+      xv[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+    }
+  }
+  if constexpr (kGamma) {
+    const uint4* gsrc = reinterpret_cast<const uint4*>(gamma + (int64_t)b * kBlock);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 gr = gsrc[i];
+      const uint32_t w[4] = {gr.x, gr.y, gr.z, gr.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[8 * i + 2 * j] *= bf16_lo(w[j]);
+        xv[8 * i + 2 * j + 1] *= bf16_hi(w[j]);
+      }
+    }
+  }
+
+  // N:M selection
+  uint32_t keep;
+  if constexpr (kGamma) {
+    uint32_t low = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) low |= __float_as_uint(xv[k]);
+    if (low & (uint32_t)(M - 1))
+      keep = select_exact<N, M>(xv);
+    else
+      keep = select_fast<N, M>(xv);
+  } else {
+    keep = select_fast<N, M>(xv);
+  }
+
+  // backbone: the block's largest |x'| is always kept (each group keeps its
+  // maximum), so the backbone scale is the block's plain MX scale
+  const uint32_t e_bb = e8m0_from_amax_bits(amax_bits32(xv));
+  const float s_bb = scale_from_e8m0(e_bb);
+  float xs[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) xs[k] = (keep >> k) & 1u ? xv[k] : 0.0f;
+  const uint4 c_bb = quantize32(xs, s_bb);
+
+  // residual against the quantised backbone (exact in fp32)
+  float q[32];
+  dequantize32(c_bb, s_bb, q);
+  float r[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) r[k] = xv[k] - q[k];
+  const uint32_t e_rs = e8m0_from_amax_bits(amax_bits32(r));
+  const uint4 c_rs = quantize32(r, scale_from_e8m0(e_rs));
+
+  const int64_t row_codes = (int64_t)blocks_per_row * (kBlock / 2);
+  reinterpret_cast<uint4*>(bb_codes + (int64_t)t * row_codes)[b] = c_bb;
+  reinterpret_cast<uint4*>(res_codes + (int64_t)t * row_codes)[b] = c_rs;
+  bb_scales[gid] = (uint8_t)e_bb;
+  res_scales[gid] = (uint8_t)e_rs;
+  if (mask_out) reinterpret_cast<uint32_t*>(mask_out)[gid] = keep;
+}
+
+// Plain MXFP4 coding of bf16 rows (the weight quantiser): same element and
+// scale rules, no mask and no residual.
+__global__ __launch_bounds__(256) void quantize_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, uint32_t blocks_per_row, uint32_t total_blocks,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total_blocks) return;
+  const uint32_t t = gid / blocks_per_row;
+  const uint32_t b = gid - t * blocks_per_row;
+  const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * ldx + (int64_t)b * kBlock);
+  float xv[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 rw = src[i];
+    const uint32_t w[4] = {rw.x, rw.y, rw.z, rw.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xv[8 * i + 2 * j] = bf16_lo(w[j]);
+      xv[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+    }
+  }
+  const uint32_t e = e8m0_from_amax_bits(amax_bits32(xv));
+  const uint4 c = quantize32(xv, scale_from_e8m0(e));
+  const int64_t row_codes = (int64_t)blocks_per_row * (kBlock / 2);
+  reinterpret_cast<uint4*>(codes + (int64_t)t * row_codes)[b] = c;
+  scales[gid] = (uint8_t)e;
+}
+
+static inline unsigned grid_for(uint32_t total, unsigned threads) {
+  return (total + threads - 1) / threads;
+}
+
+hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma,
+                          int n, int m, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
+                          uint8_t* res_scales, uint8_t* mask, hipStream_t stream) {
+  const uint32_t bpr = (uint32_t)(K / kBlock);
+  const uint32_t total = (uint32_t)(T * bpr);
+  // small problems: one wave per workgroup so that more CUs take part
+  const unsigned threads = total >= (1u << 18) ? 256 : 64;
+  const dim3 grid(grid_for(total, threads)), block(threads);
+#define SHARQ_PREP(NN, MM, GG)                                                              \
+  hipLaunchKernelGGL((prepare_kernel<NN, MM, GG>), grid, block, 0, stream, x, ldx, gamma,   \
+                     bpr, total, bb_codes, bb_scales, res_codes, res_scales, mask)
+  if (n == 2 && m == 4) {
+    if (gamma) SHARQ_PREP(2, 4, true); else SHARQ_PREP(2, 4, false);
+  } else {
+    if (gamma) SHARQ_PREP(8, 16, true); else SHARQ_PREP(8, 16, false);
+  }
+#undef SHARQ_PREP
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream) {
+  const uint32_t bpr = (uint32_t)(K / kBlock);
+  const uint32_t total = (uint32_t)(T * bpr);
+  const unsigned threads = total >= (1u << 18) ? 256 : 64;
+  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(total, threads)), dim3(threads), 0, stream, x, ldx,
+                     bpr, total, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace sharq

@@ -1,0 +1,111 @@
+// C ABI of the SharQ library: host-side argument validation (before any HIP
+// call) and dispatch to the kernel launchers.
+
+#include "../../include/sharq.h"
+#include "sharq_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? SHARQ_OK : SHARQ_EHIP; }
+
+// Shape checks shared by sharq_prepare and sharq_quantize_mxfp4.
+int check_rows(int64_t T, int64_t K, int64_t ldx) {
+  if (T < 0 || K <= 0 || K % 32 != 0 || ldx < K) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (T * (K / 32) >= ((int64_t)1 << 31)) return SHARQ_EINVAL;  // 32-bit block index
+  if (ldx % 8 != 0) return SHARQ_EALIGN;
+  return SHARQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sharq_status_string(int status) {
+  switch (status) {
+    case SHARQ_OK: return "ok";
+    case SHARQ_EINVAL: return "invalid argument (shape, stride or NULL pointer)";
+    case SHARQ_EALIGN: return "misaligned pointer or leading dimension";
+    case SHARQ_EUNSUPPORTED: return "unsupported N:M pattern (supported: 2:4, 8:16)";
+    case SHARQ_EHIP: return "HIP launch failed";
+    case SHARQ_ENOTIMPL: return "not implemented";
+    default: return "unknown status";
+  }
+}
+
+int sharq_abi_version(void) { return kAbiVersion; }
+
+int sharq_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma, int n, int m,
+                  uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes, uint8_t* res_scales, uint8_t* mask,
+                  hipStream_t stream) {
+  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
+  const int rc = check_rows(T, K, ldx);
+  if (rc != SHARQ_OK) return rc;
+  if (K % m != 0) return SHARQ_EINVAL;
+  if (T == 0) return SHARQ_OK;
+  if (!x || !bb_codes || !bb_scales || !res_codes || !res_scales) return SHARQ_EINVAL;
+  if (!aligned16(x) || (gamma && !aligned16(gamma)) || !aligned16(bb_codes) || !aligned16(bb_scales) ||
+      !aligned16(res_codes) || !aligned16(res_scales) || (mask && !aligned16(mask)))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_prepare(x, T, K, ldx, gamma, n, m, bb_codes, bb_scales, res_codes, res_scales,
+                                          mask, stream));
+}
+
+int sharq_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, uint8_t* codes, uint8_t* scales,
+                         hipStream_t stream) {
+  const int rc = check_rows(T, K, ldx);
+  if (rc != SHARQ_OK) return rc;
+  if (T == 0) return SHARQ_OK;
+  if (!x || !codes || !scales) return SHARQ_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_quantize(x, T, K, ldx, codes, scales, stream));
+}
+
+int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                 const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T, int64_t O,
+                 int64_t K, float* y, int64_t ldy, hipStream_t stream) {
+  if (T < 0 || O < 0 || K <= 0 || K % 32 != 0 || ldy < O) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (T == 0 || O == 0) return SHARQ_OK;
+  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !w_codes || !w_scales || !y) return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
+      !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y))
+    return SHARQ_EALIGN;
+  return hip_status(
+      sharq::launch_linear(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K, y, ldy, stream));
+}
+
+int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                         const uint8_t* res_scales, const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,
+                         const uint8_t* w_codes, const uint8_t* w_scales, int64_t P, int64_t O, int64_t K, float* y,
+                         hipStream_t stream) {
+  if (E < 1 || P < 0 || O < 0 || K <= 0 || K % 32 != 0) return SHARQ_EINVAL;
+  if (P >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31) ||
+      (P + 127) / 128 + E > 65535)
+    return SHARQ_EINVAL;
+  if (P == 0 || O == 0) return SHARQ_OK;
+  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !seg_offsets || !w_codes || !w_scales || !y)
+    return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
+      !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y) || !aligned16(seg_offsets) ||
+      (a_rows && !aligned16(a_rows)))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_linear_grouped(bb_codes, bb_scales, res_codes, res_scales, a_rows, seg_offsets,
+                                                 E, w_codes, w_scales, P, O, K, y, stream));
+}
+
+int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {
+  if (T < 0 || I <= 0 || I % 8 != 0) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || I >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (T * (I / 8) >= ((int64_t)1 << 32) - 256) return SHARQ_EINVAL;  // 32-bit lane index
+  if (T == 0) return SHARQ_OK;
+  if (!gu || !h) return SHARQ_EINVAL;
+  if (!aligned16(gu) || !aligned16(h)) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_silu_mul(gu, T, I, h, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// Launchers behind the C ABI. Arguments reaching these have been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sharq {
+
+hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma,
+                          int n, int m, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
+                          uint8_t* res_scales, uint8_t* mask, hipStream_t stream);
+
+hipError_t launch_quantize(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, uint8_t* codes,
+                           uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                         const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                         int64_t T, int64_t O, int64_t K, float* y, int64_t ldy, hipStream_t stream);
+
+hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                                 const uint8_t* res_codes, const uint8_t* res_scales,
+                                 const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,
+                                 const uint8_t* w_codes, const uint8_t* w_scales, int64_t P, int64_t O,
+                                 int64_t K, float* y, hipStream_t stream);
+
+hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream);
+
+}  // namespace sharq

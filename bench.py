@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Benchmark of the SharQ linear hot path on one MI355X.
+
+Default workload: a Llama-3.1-8B-shaped MLP block at 2048-token prefill, 2:4,
+MXFP4, RMSNorm gamma absorbed in the first prepare:
+    prepare(x, gamma) -> two-path GEMM gate|up [28672 x 4096] -> silu_mul
+    -> prepare(h) -> two-path GEMM down [4096 x 14336]
+One step = one pass of that chain over 2048 tokens. Inputs are seeded synthetic
+data resident in HBM before the timed region; weights are quantised once on
+the GPU (not timed).
+
+Prints ONE JSON line with tokens/s, the per-stage breakdown (HIP events on the
+launch stream), the roofline of the dominant kernel and the CPU oracle timed on
+a bounded sample of the same workload. Other workloads: --workload NAME.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 scaled MFMA
+
+WORKLOADS = ["llama8b_mlp", "linear_128x4096", "down_8of16", "down_2of4", "llama70b_decode_T1",
+             "llama70b_decode_T8", "llama70b_decode_T32", "llama70b_decode_T64", "qwen3_moe"]
+
+
+def prepare_bytes(T, K, gamma=False):
+    """Algorithmic HBM bytes of one prepare: read bf16 x (2/elem) + gamma, write two code
+    arrays (0.5/elem each), two scale arrays (1/32 each) and the mask (1/8)."""
+    return T * K * (2 + 0.5 + 0.5 + 2 / 32 + 1 / 8) + (2 * K if gamma else 0)
+
+
+def gemm_flops(T, O, K, n=2, m=4):
+    """(algorithmic, executed) flops of the two-path GEMM: the backbone holds n/m of K."""
+    return 2.0 * T * O * K * (1 + n / m), 4.0 * T * O * K
+
+
+def gemm_bytes(T, O, K):
+    """Minimum HBM bytes of one two-path GEMM: both A operands, W once, fp32 Y."""
+    return 2 * T * K * 17 / 32 + O * K * 17 / 32 + 4 * T * O
+
+
+def silu_bytes(T, I):
+    return T * (8 * I + 2 * I)
+
+
+def _to_gpu_bf16(torch, u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class Stage:
+    def __init__(self, name, fn, kind, bytes_=0.0, flops_alg=0.0, flops_exec=0.0):
+        self.name, self.fn, self.kind = name, fn, kind
+        self.bytes, self.flops_alg, self.flops_exec = bytes_, flops_alg, flops_exec
+
+
+def build_workload(name, torch, sq):
+    """Returns (stages, tokens_per_step, config dict, oracle sample fn)."""
+    from synth import (workload_down_silu, workload_linear, workload_llama70b_decode, workload_llama8b_mlp,
+                       workload_qwen3_moe)
+    if name == "llama8b_mlp":
+        wl = workload_llama8b_mlp()
+        T, H, I = wl["x"].shape[0], wl["hidden"], wl["inter"]
+        x, g = _to_gpu_bf16(torch, wl["x"]), _to_gpu_bf16(torch, wl["gamma"])
+        w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"]))
+        w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"]))
+        buf = {}
+        buf["p1"] = sq.prepare(x, g, 2, 4)
+        buf["gu"] = sq.linear(buf["p1"], w_gu)
+        buf["h"] = sq.silu_mul(buf["gu"])
+        buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
+        buf["y"] = sq.linear(buf["p2"], w_dn)
+        fa1, fe1 = gemm_flops(T, 2 * I, H)
+        fa2, fe2 = gemm_flops(T, H, I)
+        stages = [
+            Stage("prepare_x_gamma", lambda: sq.prepare(x, g, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(T, H, True)),
+            Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "mfma", gemm_bytes(T, 2 * I, H),
+                  fa1, fe1),
+            Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
+            Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm", prepare_bytes(T, I)),
+            Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "mfma", gemm_bytes(T, H, I), fa2, fe2),
+        ]
+        cfg = {"workload": "Llama-3.1-8B MLP block, 2048-token prefill, 2:4, MXFP4, RMSNorm gamma absorbed",
+               "tokens": T, "hidden": H, "intermediate": I, "nm": "2:4", "seed": 1002}
+
+        def oracle_sample(rows):
+            from oracle import linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref
+            xs = wl["x"][:rows]
+            t0 = time.perf_counter()
+            p1 = prepare_ref(xs, wl["gamma"], 2, 4)
+            wc, ws = quantize_weight_ref(wl["w_gu"])
+            gu, _ = linear_ref(p1["bb_codes"], p1["bb_scales"], p1["res_codes"], p1["res_scales"], wc, ws)
+            h = silu_mul_ref(gu.astype(np.float32), I)
+            p2 = prepare_ref(h, None, 2, 4)
+            wc, ws = quantize_weight_ref(wl["w_down"])
+            linear_ref(p2["bb_codes"], p2["bb_scales"], p2["res_codes"], p2["res_scales"], wc, ws)
+            return time.perf_counter() - t0
+        return stages, T, cfg, oracle_sample
+
+    if name == "linear_128x4096" or name.startswith("down_"):
+        if name == "linear_128x4096":
+            wl = workload_linear()
+            xb, wb, n, m = wl["x"], wl["w"], 2, 4
+            label = "single linear 128x4096 -> 4096, 2:4, MXFP4"
+        else:
+            wl = workload_down_silu()
+            xb, wb = wl["x"], wl["w"]
+            n, m = (8, 16) if name == "down_8of16" else (2, 4)
+            label = f"down_proj 2048x14336 -> 4096, {n}:{m}, MXFP4, SiLU-gated input"
+        T, K = xb.shape
+        O = wb.shape[0]
+        x = _to_gpu_bf16(torch, xb)
+        wq = sq.quantize_mxfp4(_to_gpu_bf16(torch, wb))
+        buf = {"p": sq.prepare(x, None, n, m)}
+        buf["y"] = sq.linear(buf["p"], wq)
+        fa, fe = gemm_flops(T, O, K, n, m)
+        stages = [Stage("prepare", lambda: sq.prepare(x, None, n, m, out=buf["p"]), "hbm", prepare_bytes(T, K)),
+                  Stage("gemm", lambda: sq.linear(buf["p"], wq, out=buf["y"]), "mfma", gemm_bytes(T, O, K), fa, fe)]
+        cfg = {"workload": label, "tokens": T, "in_features": K, "out_features": O, "nm": f"{n}:{m}"}
+
+        def oracle_sample(rows):
+            from oracle import linear_ref, prepare_ref, quantize_weight_ref
+            t0 = time.perf_counter()
+            p = prepare_ref(xb[:rows], None, n, m)
+            wc, ws = quantize_weight_ref(wb)
+            linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
+            return time.perf_counter() - t0
+        return stages, T, cfg, oracle_sample
+
+    if name.startswith("llama70b_decode_T"):
+        T = int(name.split("_T")[1])
+        wl = workload_llama70b_decode(T)
+        H, I = wl["hidden"], wl["inter"]
+        x = _to_gpu_bf16(torch, wl["x"])
+        w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"]))
+        w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"]))
+        buf = {"p1": sq.prepare(x, None, 2, 4)}
+        buf["gu"] = sq.linear(buf["p1"], w_gu)
+        buf["h"] = sq.silu_mul(buf["gu"])
+        buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
+        buf["y"] = sq.linear(buf["p2"], w_dn)
+        fa1, fe1 = gemm_flops(T, 2 * I, H)
+        fa2, fe2 = gemm_flops(T, H, I)
+        stages = [
+            Stage("prepare_x", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(T, H)),
+            Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "hbm", gemm_bytes(T, 2 * I, H),
+                  fa1, fe1),
+            Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
+            Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm", prepare_bytes(T, I)),
+            Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "hbm", gemm_bytes(T, H, I), fa2, fe2),
+        ]
+        cfg = {"workload": f"Llama-3.1-70B MLP decode, {T} tokens, 2:4, MXFP4", "tokens": T, "hidden": H,
+               "intermediate": I, "nm": "2:4"}
+        return stages, T, cfg, None
+
+    if name == "qwen3_moe":
+        wl = workload_qwen3_moe()
+        E, I, H = wl["experts"], wl["inter"], wl["hidden"]
+        P = len(wl["a_rows"])
+        tokens = wl["x"].shape[0]
+        x = _to_gpu_bf16(torch, wl["x"])
+        wg = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"].reshape(E * 2 * I, H)))
+        wd = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"].reshape(E * H, I)))
+        w_gu = sq.MXFP4(wg.codes.view(E, 2 * I, H // 2), wg.scales.view(E, 2 * I, H // 32))
+        w_dn = sq.MXFP4(wd.codes.view(E, H, I // 2), wd.scales.view(E, H, I // 32))
+        seg = torch.from_numpy(wl["seg_offsets"]).cuda()
+        rows = torch.from_numpy(wl["a_rows"]).cuda()
+        buf = {"p1": sq.prepare(x, None, 2, 4)}
+        buf["gu"] = sq.linear_grouped(buf["p1"], w_gu, seg, rows)
+        buf["h"] = sq.silu_mul(buf["gu"])
+        buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
+        buf["y"] = sq.linear_grouped(buf["p2"], w_dn, seg, None)
+        fa1, fe1 = gemm_flops(P, 2 * I, H)
+        fa2, fe2 = gemm_flops(P, H, I)
+        stages = [
+            Stage("prepare_tokens", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(tokens, H)),
+            Stage("grouped_gate_up", lambda: sq.linear_grouped(buf["p1"], w_gu, seg, rows, out=buf["gu"]), "hbm",
+                  2 * P * H * 17 / 32 + E * 2 * I * H * 17 / 32 + 4 * P * 2 * I, fa1, fe1),
+            Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(P, I)),
+            Stage("prepare_pairs", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm", prepare_bytes(P, I)),
+            Stage("grouped_down", lambda: sq.linear_grouped(buf["p2"], w_dn, seg, None, out=buf["y"]), "hbm",
+                  2 * P * I * 17 / 32 + E * H * I * 17 / 32 + 4 * P * H, fa2, fe2),
+        ]
+        cfg = {"workload": "Qwen3-30B-A3B MoE expert layer, 4096 tokens, top-8 of 128, 2:4, MXFP4",
+               "tokens": tokens, "pairs": P, "experts": E, "hidden": H, "intermediate": I, "nm": "2:4"}
+        return stages, tokens, cfg, None
+
+    raise SystemExit(f"unknown workload {name}; choose from {WORKLOADS}")
+
+
+def cpu_baseline(oracle_sample, tokens_full, budget_s=20.0):
+    """Time the CPU oracle on a bounded row sample; grow the sample until it takes
+    a few seconds, stop before the budget."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+        blas_name = blas[0].get("internal_api", "?") if blas else "?"
+    except Exception:
+        threads, blas_name = os.cpu_count() or 1, "?"
+    rows, spent = 4, 0.0
+    while True:
+        dt = oracle_sample(rows)
+        spent += dt
+        if dt > budget_s / 4 or rows * 2 > tokens_full or spent + 2.5 * dt > budget_s:
+            break
+        rows *= 2
+    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows} of {tokens_full} tokens through the numpy/fp64 oracle of the same chain "
+                      f"(weights quantised inside the timed call), {dt:.2f} s; BLAS {blas_name} with {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b_mlp", choices=WORKLOADS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import activation_sparsity_fp4_amd as sq
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs the GPU")
+    torch.cuda.init()
+    print(f"# building inputs for {args.workload}", file=sys.stderr, flush=True)
+    stages, tokens, cfg, oracle_sample = build_workload(args.workload, torch, sq)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for s in stages:
+            s.fn()
+    torch.cuda.synchronize()
+    print(f"# warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    n = len(stages)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev = events[k]
+        ev[0].record()
+        for i, s in enumerate(stages):
+            s.fn()
+            ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_per_step = 1e3 * wall / args.steps
+    stage_ms = [float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+                for i in range(n)]
+    breakdown = {}
+    for s, ms in zip(stages, stage_ms):
+        d = {"us": round(ms * 1e3, 2)}
+        if s.bytes:
+            d["GB/s"] = round(s.bytes / (ms * 1e-3) / 1e9, 1)
+            d["hbm_frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
+        if s.flops_alg:
+            d["TFLOP/s_alg"] = round(s.flops_alg / (ms * 1e-3) / 1e12, 1)
+            d["TFLOP/s_exec"] = round(s.flops_exec / (ms * 1e-3) / 1e12, 1)
+            d["mfma_frac_alg"] = round(d["TFLOP/s_alg"] / FP4_PEAK_TFLOPS, 4)
+        breakdown[s.name] = d
+
+    # dominant kernel: the stage with the largest average duration
+    dom_i = int(np.argmax(stage_ms))
+    dom = stages[dom_i]
+    if dom.kind == "mfma":
+        ach = dom.flops_alg / (stage_ms[dom_i] * 1e-3) / 1e12
+        roof = {"kernel": dom.name, "bound": "mfma", "achieved": round(ach, 1), "peak": FP4_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP4_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        ach = dom.bytes / (stage_ms[dom_i] * 1e-3) / 1e9
+        roof = {"kernel": dom.name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+
+    value = tokens * args.steps / wall
+    line = {
+        "metric": "SharQ linear tokens/s (prepare GB/s and FP4 GEMM TFLOP/s as fractions of MI355X peak)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4", "data": "synthetic", "config": cfg, "roofline": roof, "stages": breakdown,
+    }
+    if oracle_sample is not None and not args.no_cpu_baseline:
+        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(oracle_sample, tokens)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

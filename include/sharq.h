@@ -1,0 +1,148 @@
+/*
+ * sharq.h -- C ABI of the SharQ linear hot path on AMD MI355X (gfx950).
+ *
+ * The method (page "SharQ: Bridging Activation Sparsity and FP4 Quantization
+ * for LLM Inference", Abstract and Section 1): for each activation row an
+ * online N:M mask keeps the N largest |x| of every M consecutive entries along
+ * K; that outlier-dominated sparse backbone is quantised to block-scaled FP4;
+ * a dense residual is taken against the *quantised* backbone and quantised to
+ * FP4 with its own scales; a sparse FP4 GEMM on the backbone and a dense FP4
+ * GEMM on the residual share one FP4 weight and accumulate into one output.
+ *
+ * FP4 format (MXFP4, the OCP MX format named in Section 2.3 of that page):
+ * E2M1 codes {0, .5, 1, 1.5, 2, 3, 4, 6} with bit 3 the sign, two codes per
+ * byte with the even K index in the low nibble; one E8M0 scale byte
+ * (exponent + 127) per 32 consecutive K entries; exponent
+ * floor(log2(block amax)) - 2, clamped to [-127, 127], -127 for an all-zero
+ * block; codes round to nearest with ties to the even code and saturate at 6.
+ *
+ * Conventions for every entry point below:
+ *  - Pointers are DEVICE pointers unless stated otherwise; the caller owns
+ *    every buffer; the library allocates nothing and keeps no state, so calls
+ *    are re-entrant.
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *  - Arguments are validated on the host before any HIP call. Errors return a
+ *    negative sharq_status and enqueue nothing. A fault inside a kernel shows
+ *    up at the caller's next synchronisation (the HIP convention).
+ *  - A call with no rows (T, P or O equal to 0) is a no-op that returns
+ *    SHARQ_OK once the shape arguments are valid; its pointers may be NULL.
+ *  - Inputs must be finite; with NaN or Inf the outputs are unspecified.
+ *  - Row-major layouts; sizes are element counts. T = rows (tokens),
+ *    K = input features, O = output features.
+ *  - Alignment: every pointer 16-byte aligned; ldx a multiple of 8.
+ */
+#ifndef SHARQ_H
+#define SHARQ_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifndef SHARQ_API
+#define SHARQ_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SHARQ_OK = 0,
+  SHARQ_EINVAL = -1,       /* bad shape, stride or NULL pointer */
+  SHARQ_EALIGN = -2,       /* pointer not 16-byte aligned, or ldx % 8 != 0 */
+  SHARQ_EUNSUPPORTED = -3, /* (n, m) not in {(2,4), (8,16)} */
+  SHARQ_EHIP = -4,         /* the HIP launch itself failed */
+  SHARQ_ENOTIMPL = -5      /* a shape class this build does not handle */
+} sharq_status;
+
+/* Host. Static string describing a status code; never NULL. */
+SHARQ_API const char* sharq_status_string(int status);
+
+/* Host. Version of this ABI (bumped on any signature change). */
+SHARQ_API int sharq_abi_version(void);
+
+/*
+ * sharq_prepare -- the fused prepare operator (SharQ page, Abstract: mask
+ * generation, residual construction and layer-norm absorption in one
+ * operator; Section 1: the residual is taken against the quantised backbone).
+ *
+ *  x        bf16 [T][ldx], the first K entries of each row are used.
+ *  gamma    bf16 [K] RMSNorm weight absorbed as x' = x * gamma (fp32), or NULL.
+ *  n, m     N:M pattern: (2,4) or (8,16). Selection keeps, in each group of m
+ *           consecutive K entries, the n largest |x'|; equal |x'| go to the
+ *           lower index.
+ *  bb_codes   u8 [T][K/2]   backbone E2M1 codes (0x0 at dropped positions)
+ *  bb_scales  u8 [T][K/32]  backbone E8M0 scales
+ *  res_codes  u8 [T][K/2]   residual codes, residual r = x' - dequant(backbone)
+ *  res_scales u8 [T][K/32]  residual scales
+ *  mask       u8 [T][K/8]   bit (k & 7) of byte k >> 3 set when k is kept, or
+ *                           NULL to skip writing it.
+ * Requires K % 32 == 0, K % m == 0, T >= 0 (T == 0 is a no-op), ldx >= K,
+ * T * K / 32 < 2^31.
+ */
+SHARQ_API int sharq_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx,
+                  const uint16_t* gamma, int n, int m,
+                  uint8_t* bb_codes, uint8_t* bb_scales,
+                  uint8_t* res_codes, uint8_t* res_scales,
+                  uint8_t* mask, hipStream_t stream);
+
+/*
+ * sharq_quantize_mxfp4 -- plain MXFP4 of bf16 rows along K (no mask, no
+ * residual), the same element and scale rules as sharq_prepare. Used to
+ * produce the pre-quantised weight [O][K] that sharq_linear reads.
+ *  x bf16 [T][ldx]; codes u8 [T][K/2]; scales u8 [T][K/32].
+ * Requires K % 32 == 0, ldx >= K, T * K / 32 < 2^31.
+ */
+SHARQ_API int sharq_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx,
+                         uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/*
+ * sharq_linear -- the two-path FP4 GEMM (SharQ page, Abstract: a sparse FP4
+ * GEMM on the backbone and a dense FP4 GEMM on the residual share one FP4
+ * weight load; Section 1: the residual path accumulates into the sparse
+ * output):
+ *   Y[t][o] = sum_k deq(bb)[t][k] * deq(W)[o][k] + sum_k deq(res)[t][k] * deq(W)[o][k]
+ *  bb_codes/res_codes u8 [T][K/2], bb_scales/res_scales u8 [T][K/32] (as
+ *  written by sharq_prepare); w_codes u8 [O][K/2], w_scales u8 [O][K/32];
+ *  y fp32 [T][ldy], overwritten (not accumulated into).
+ * Accumulation is fp32 in an unspecified order. Requires K % 32 == 0,
+ * ldy >= O, T >= 0 (T == 0 or O == 0 is a no-op).
+ */
+SHARQ_API int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                 const uint8_t* res_codes, const uint8_t* res_scales,
+                 const uint8_t* w_codes, const uint8_t* w_scales,
+                 int64_t T, int64_t O, int64_t K, float* y, int64_t ldy,
+                 hipStream_t stream);
+
+/*
+ * sharq_linear_grouped -- sharq_linear per expert segment, for mixture-of-
+ * experts layers (SharQ page, Abstract: MoE models are among the targets).
+ * Output row p (0 <= p < P) belongs to the expert e with
+ * seg_offsets[e] <= p < seg_offsets[e+1]; it reads activation row a_rows[p]
+ * (or row p when a_rows is NULL) and expert e's weight.
+ *  a_rows      i32 [P] device, each in [0, T_src), or NULL.
+ *  seg_offsets i32 [E+1] device, non-decreasing, [0] = 0, [E] = P.
+ *  w_codes u8 [E][O][K/2], w_scales u8 [E][O][K/32]; y fp32 [P][O].
+ * Segment contents are read on the device; their validity is a precondition.
+ */
+SHARQ_API int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                         const uint8_t* res_codes, const uint8_t* res_scales,
+                         const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         int64_t P, int64_t O, int64_t K, float* y,
+                         hipStream_t stream);
+
+/*
+ * sharq_silu_mul -- glue between a fused gate|up projection and the down
+ * projection (not part of the method): h[t][i] = bf16(silu(g) * u) with
+ * g = gu[t][i], u = gu[t][I + i], silu(g) = g / (1 + exp(-g)), fp32 math,
+ * round-to-nearest-even to bf16.
+ *  gu fp32 [T][2I]; h bf16 [T][I]. Requires I % 8 == 0.
+ */
+SHARQ_API int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h,
+                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHARQ_H */

@@ -38,6 +38,7 @@ __all__ = [
     "workload_qwen3_moe",
     "moe_routing",
     "array_digest",
+    "adversarial_rows",
 ]
 
 SEEDS = {
@@ -182,3 +183,28 @@ def workload_qwen3_moe(seed: int = SEEDS["qwen3_moe"], tokens: int = 4096, hidde
 def array_digest(a: np.ndarray) -> str:
     """Short SHA-256 of an array's bytes (recorded next to bench results)."""
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()[:16]
+
+
+def adversarial_rows(K: int, seed: int = 0) -> np.ndarray:
+    """float32 rows [10 x K] that stress edge cases: zeros, alternating +-0, constant
+    rows (all ties), bf16 subnormals, small-alphabet ties, mixed normal/subnormal,
+    huge outliers, values near the fp32 range, powers of two over the whole bf16
+    exponent range, and values that land between 6 and 8 after block scaling."""
+    rng = np.random.default_rng(seed)
+    rows = [
+        np.zeros(K),
+        np.where(np.arange(K) % 2, -0.0, 0.0),
+        np.full(K, 1.5),
+        np.full(K, -2.0 ** -130),
+        rng.choice([1.0, -1.0, 2.0, 0.0], size=K),
+        rng.standard_normal(K) * 2.0 ** -128,
+    ]
+    big = rng.standard_normal(K)
+    big[::13] *= 1e30
+    rows.append(big)
+    rows.append(rng.standard_normal(K) * 1e37)
+    rows.append(np.ldexp(1.0, rng.integers(-133, 127, K)) * rng.choice([-1, 1], K))
+    sat = rng.standard_normal(K)
+    sat[::32] = 7.0
+    rows.append(sat)
+    return np.array(rows, dtype=np.float32)

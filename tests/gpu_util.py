@@ -1,0 +1,94 @@
+"""Helpers for the GPU parity tests: host <-> device copies and the Y tolerance."""
+
+import numpy as np
+
+TOL_REL = 1e-4
+TOL_ABS = 1e-6
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev():
+    return torch().device("cuda:0")
+
+
+def bf16_to_gpu(u16):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(u16, dtype=np.uint16).view(np.int16)).view(t.bfloat16).to(dev())
+
+
+def u8_to_gpu(a):
+    return torch().from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev())
+
+
+def i32_to_gpu(a):
+    return torch().from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+
+
+def f32_to_gpu(a):
+    return torch().from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev())
+
+
+def to_np(t):
+    tt = torch()
+    t = t.detach().cpu()
+    if t.dtype == tt.bfloat16:
+        return t.view(tt.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def oracle_prepared(out):
+    """Upload an oracle prepare result as the GPU's Prepared tuple."""
+    import activation_sparsity_fp4_amd as sq
+    return sq.Prepared(u8_to_gpu(out["bb_codes"]), u8_to_gpu(out["bb_scales"]), u8_to_gpu(out["res_codes"]),
+                       u8_to_gpu(out["res_scales"]), None)
+
+
+def assert_prepare_equal(got, want, rows=None):
+    """Bit-exact comparison of a GPU Prepared against an oracle dict (optionally on a row subset)."""
+    for name in ("bb_codes", "bb_scales", "res_codes", "res_scales", "mask"):
+        g = getattr(got, name)
+        if g is None:
+            continue
+        g = to_np(g)
+        if rows is not None:
+            g = g[rows]
+        w = want[name]
+        if not np.array_equal(g, w):
+            bad = np.argwhere(g != w)
+            r, c = bad[0]
+            raise AssertionError(f"{name}: {len(bad)} mismatches, first at row {r} col {c}: "
+                                 f"gpu {g[r, c]:#x} oracle {w[r, c]:#x}")
+
+
+def assert_y_close(y_gpu, y_ref, bound):
+    """|Y_gpu - Y_ref| <= 1e-4 * sum_k |a_k w_k| + 1e-6 elementwise."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64)
+    err = np.abs(y_gpu - y_ref)
+    tol = TOL_REL * bound + TOL_ABS
+    bad = err > tol
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{bad.sum()} of {bad.size} outside tolerance; first {tuple(i)}: gpu {y_gpu[tuple(i)]} "
+                             f"ref {y_ref[tuple(i)]} tol {tol[tuple(i)]}")
+    return float((err / np.maximum(tol, 1e-30)).max())
+
+
+def assert_bf16_close(h, want):
+    """bf16 outputs of fp32 math against the correctly rounded value: within one
+    bf16 ulp (same sign), or both below 2^-126 in magnitude, where fp32
+    intermediate results (exp overflow in silu) legitimately flush to zero."""
+    from synth import bf16_to_f32
+    h = np.asarray(h, dtype=np.uint16)
+    want = np.asarray(want, dtype=np.uint16)
+    diff = np.abs(h.astype(np.int32) - want.astype(np.int32))
+    same_sign = (h >> 15) == (want >> 15)
+    tiny = (np.abs(bf16_to_f32(h)) < 2.0 ** -126) & (np.abs(bf16_to_f32(want)) < 2.0 ** -126)
+    ok = ((diff <= 1) & same_sign) | tiny
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{(~ok).sum()} bf16 values off by more than one ulp; first {i}: "
+                             f"gpu {h[i]:#06x} want {want[i]:#06x}")

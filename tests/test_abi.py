@@ -1,0 +1,127 @@
+"""The C-ABI library loads on the host, exports every entry point the header
+declares, and rejects bad arguments before any HIP call (CPU only: no call
+here reaches a kernel launch)."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from activation_sparsity_fp4_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sharq.h")
+
+A = 0x10000  # fake, 16-byte aligned device addresses: never dereferenced
+B = 0x20000
+C = 0x30000
+D = 0x40000
+E_ = 0x50000
+F = 0x60000
+G = 0x70000
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SHARQ_API[^;]*?\b(sharq_\w+)\s*\(", text, flags=re.S)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(declared_symbols()) == exported
+
+
+def test_status_strings_and_version():
+    assert _lib.call("sharq_abi_version") == 1
+    for s in (0, -1, -2, -3, -4, -5):
+        assert _lib.status_string(s)
+    assert _lib.status_string(-99) == "unknown status"
+
+
+def prep(x=A, T=4, K=64, ldx=64, gamma=0, n=2, m=4, bc=B, bs=C, rc=D, rs=E_, mask=F):
+    return _lib.call("sharq_prepare", x, T, K, ldx, gamma, n, m, bc, bs, rc, rs, mask, 0)
+
+
+def test_prepare_validation():
+    assert prep(T=0) == _lib.SHARQ_OK  # no-op, no launch
+    assert prep(x=0) == _lib.SHARQ_EINVAL
+    assert prep(bc=0) == _lib.SHARQ_EINVAL
+    assert prep(rs=0) == _lib.SHARQ_EINVAL
+    assert prep(T=-1) == _lib.SHARQ_EINVAL
+    assert prep(K=48, ldx=48) == _lib.SHARQ_EINVAL      # K % 32
+    assert prep(K=0, ldx=0) == _lib.SHARQ_EINVAL
+    assert prep(ldx=32) == _lib.SHARQ_EINVAL            # ldx < K
+    assert prep(n=4, m=8) == _lib.SHARQ_EUNSUPPORTED
+    assert prep(n=1, m=4) == _lib.SHARQ_EUNSUPPORTED
+    assert prep(x=A + 2) == _lib.SHARQ_EALIGN
+    assert prep(ldx=68) == _lib.SHARQ_EALIGN
+    assert prep(gamma=G + 4) == _lib.SHARQ_EALIGN
+    assert prep(mask=F + 8) == _lib.SHARQ_EALIGN
+    assert prep(T=1 << 31) == _lib.SHARQ_EINVAL
+    assert prep(T=1 << 26, K=1024, ldx=1024) == _lib.SHARQ_EINVAL  # too many blocks for 32-bit indexing
+
+
+def test_prepare_k_multiple_of_m():
+    # K = 96 is a multiple of 32 and of 16, so 8:16 accepts it (T = 0 keeps it a no-op)
+    assert prep(n=8, m=16, K=96, ldx=96, T=0) == _lib.SHARQ_OK
+
+
+def lin(T=4, O=8, K=64, y=G, ldy=8, **kw):
+    args = dict(bc=A, bs=B, rc=C, rs=D, wc=E_, ws=F)
+    args.update(kw)
+    return _lib.call("sharq_linear", args["bc"], args["bs"], args["rc"], args["rs"], args["wc"], args["ws"],
+                     T, O, K, y, ldy, 0)
+
+
+def test_linear_validation():
+    assert lin(T=0) == _lib.SHARQ_OK
+    assert lin(O=0, ldy=0) == _lib.SHARQ_OK
+    assert lin(y=0) == _lib.SHARQ_EINVAL
+    assert lin(wc=0) == _lib.SHARQ_EINVAL
+    assert lin(K=48) == _lib.SHARQ_EINVAL
+    assert lin(ldy=4) == _lib.SHARQ_EINVAL
+    assert lin(T=-3) == _lib.SHARQ_EINVAL
+    assert lin(ws=F + 1) == _lib.SHARQ_EALIGN
+    assert lin(y=G + 4) == _lib.SHARQ_EALIGN
+
+
+def grp(P=16, O=8, K=64, E=2, a_rows=A, seg=B, **kw):
+    return _lib.call("sharq_linear_grouped", C, D, E_, F, a_rows, seg, E, G, G + 4096, P, O, K, 0x90000, 0)
+
+
+def test_grouped_validation():
+    assert grp(P=0) == _lib.SHARQ_OK
+    assert grp(E=0) == _lib.SHARQ_EINVAL
+    assert grp(seg=0) == _lib.SHARQ_EINVAL
+    assert grp(K=40) == _lib.SHARQ_EINVAL
+    assert grp(a_rows=A + 4) == _lib.SHARQ_EALIGN
+    assert grp(P=1 << 24, E=1) == _lib.SHARQ_EINVAL  # grid bound
+
+
+def test_silu_and_quantize_validation():
+    assert _lib.call("sharq_silu_mul", A, 0, 16, B, 0) == _lib.SHARQ_OK
+    assert _lib.call("sharq_silu_mul", A, 4, 12, B, 0) == _lib.SHARQ_EINVAL
+    assert _lib.call("sharq_silu_mul", 0, 4, 16, B, 0) == _lib.SHARQ_EINVAL
+    assert _lib.call("sharq_silu_mul", A + 4, 4, 16, B, 0) == _lib.SHARQ_EALIGN
+    assert _lib.call("sharq_quantize_mxfp4", A, 0, 64, 64, B, C, 0) == _lib.SHARQ_OK
+    assert _lib.call("sharq_quantize_mxfp4", A, 2, 64, 64, 0, C, 0) == _lib.SHARQ_EINVAL
+    assert _lib.call("sharq_quantize_mxfp4", A, 2, 50, 64, B, C, 0) == _lib.SHARQ_EINVAL
+    assert _lib.call("sharq_quantize_mxfp4", A, 2, 64, 64, B, C + 1, 0) == _lib.SHARQ_EALIGN
+
+
+def test_python_wrappers_refuse_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import activation_sparsity_fp4_amd as sq
+    with pytest.raises(ValueError):
+        sq.prepare(torch.zeros((2, 64), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        sq.silu_mul(torch.zeros((2, 16), dtype=torch.float32))

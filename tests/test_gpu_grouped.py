@@ -1,0 +1,154 @@
+"""GPU parity of the grouped two-path GEMM (MoE experts) and of the SiLU glue,
+and the chained MLP blocks, against the oracle.
+
+Chained stages: the oracle of a later stage is fed the GPU's output of the
+previous stage (its bf16 h), so prepare checks stay bit-exact while Y is only
+checked to tolerance; every stage is compared against the oracle separately.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import (linear_grouped_ref, linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref)
+from synth import bf16_round, bf16_to_f32, moe_routing, workload_llama8b_mlp, workload_qwen3_moe
+from gpu_util import (assert_bf16_close, assert_prepare_equal, assert_y_close, bf16_to_gpu, f32_to_gpu,
+                      i32_to_gpu, oracle_prepared, to_np, u8_to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import activation_sparsity_fp4_amd as sq
+    return sq
+
+
+def _experts(E, O, K, rng):
+    wq = [quantize_weight_ref(bf16_round((rng.standard_normal((O, K)) * 0.02).astype(np.float32)))
+          for _ in range(E)]
+    return np.stack([c for c, _ in wq]), np.stack([s for _, s in wq])
+
+
+@pytest.mark.parametrize("use_rows", [True, False])
+def test_grouped_small_with_empty_and_single_row_experts(sq, use_rows):
+    print(f"grouped small a_rows={use_rows}", flush=True)
+    rng = np.random.default_rng(21)
+    tokens, E, K, O = 300, 7, 256, 96
+    x = bf16_round((rng.standard_normal((tokens, K)) * 3).astype(np.float32))
+    p = prepare_ref(x, None, 2, 4)
+    wc, ws = _experts(E, O, K, rng)
+    if use_rows:
+        a_rows, seg, _, _ = moe_routing(rng, tokens, E, 2)
+        # reshape the segments: expert 2 empty, expert 4 a single row
+        P = len(a_rows)
+        seg = np.array([0, 150, 300, 300, 420, 421, 500, P], np.int32)
+    else:
+        a_rows = None
+        P = tokens
+        seg = np.array([0, 1, 1, 130, 131, 260, 299, P], np.int32)
+    y = sq.linear_grouped(oracle_prepared(p), sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws)), i32_to_gpu(seg),
+                          None if a_rows is None else i32_to_gpu(a_rows))
+    y_ref, bound = linear_grouped_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], a_rows, seg,
+                                      wc, ws)
+    assert_y_close(to_np(y), y_ref, bound)
+
+
+def test_silu_mul(sq):
+    print("silu_mul", flush=True)
+    rng = np.random.default_rng(3)
+    T, I = 67, 200
+    gu = (rng.standard_normal((T, 2 * I)) * rng.lognormal(0, 1, (T, 1)) * 3).astype(np.float32)
+    gu[0, :8] = [0, -0.0, 80, -80, 1e-30, -1e-30, 1e4, -1e4]
+    h = to_np(sq.silu_mul(f32_to_gpu(gu)))
+    want = silu_mul_ref(gu, I)
+    assert_bf16_close(h, want)
+
+
+def _sample(n, count, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(count, n), replace=False)]))
+
+
+def test_llama8b_mlp_block_chain(sq):
+    """prepare(x, gamma) -> gate|up -> silu_mul -> prepare(h) -> down at full size."""
+    print("chained llama8b MLP block", flush=True)
+    wl = workload_llama8b_mlp()
+    I = wl["inter"]
+    xg = bf16_to_gpu(wl["x"])
+    w_gu = sq.quantize_mxfp4(bf16_to_gpu(wl["w_gu"]))
+    w_dn = sq.quantize_mxfp4(bf16_to_gpu(wl["w_down"]))
+    p1 = sq.prepare(xg, bf16_to_gpu(wl["gamma"]), 2, 4)
+    gu = sq.linear(p1, w_gu)
+    h = sq.silu_mul(gu)
+    p2 = sq.prepare(h, None, 2, 4)
+    y = sq.linear(p2, w_dn)
+    rows = _sample(2048, 24, 7)
+    # stage 1: prepare with gamma
+    o1 = prepare_ref(wl["x"][rows], wl["gamma"], 2, 4)
+    assert_prepare_equal(p1, o1, rows=rows)
+    # stage 2: gate|up on sampled columns, both halves
+    cols = np.concatenate([_sample(I, 96, 8), I + _sample(I, 96, 9)])
+    wc, ws = quantize_weight_ref(wl["w_gu"][cols])
+    y_ref, bound = linear_ref(o1["bb_codes"], o1["bb_scales"], o1["res_codes"], o1["res_scales"], wc, ws)
+    gu_np = to_np(gu)
+    assert_y_close(gu_np[np.ix_(rows, cols)], y_ref, bound)
+    # stage 3: silu_mul of the GPU's gate|up rows
+    h_np = to_np(h)
+    want_h = silu_mul_ref(gu_np[rows], I)
+    assert_bf16_close(h_np[rows], want_h)
+    # stage 4: prepare of the GPU's h (bit-exact)
+    o2 = prepare_ref(h_np[rows], None, 2, 4)
+    assert_prepare_equal(p2, o2, rows=rows)
+    # stage 5: down projection on sampled columns
+    dcols = _sample(4096, 256, 10)
+    wc, ws = quantize_weight_ref(wl["w_down"][dcols])
+    y_ref, bound = linear_ref(o2["bb_codes"], o2["bb_scales"], o2["res_codes"], o2["res_scales"], wc, ws)
+    assert_y_close(to_np(y)[np.ix_(rows, dcols)], y_ref, bound)
+
+
+def test_qwen3_moe_layer_chain(sq):
+    """prepare(tokens) -> grouped gate|up (gathered rows) -> silu_mul -> prepare(pairs) -> grouped down."""
+    print("chained qwen3 MoE expert layer", flush=True)
+    import torch
+    wl = workload_qwen3_moe()
+    E, I, H = wl["experts"], wl["inter"], wl["hidden"]
+    a_rows, seg = wl["a_rows"], wl["seg_offsets"]
+    P = len(a_rows)
+    w_gu = sq.quantize_mxfp4(bf16_to_gpu(wl["w_gu"].reshape(E * 2 * I, H)))
+    w_dn = sq.quantize_mxfp4(bf16_to_gpu(wl["w_down"].reshape(E * H, I)))
+    w_gu = sq.MXFP4(w_gu.codes.view(E, 2 * I, H // 2), w_gu.scales.view(E, 2 * I, H // 32))
+    w_dn = sq.MXFP4(w_dn.codes.view(E, H, I // 2), w_dn.scales.view(E, H, I // 32))
+    seg_g, rows_g = i32_to_gpu(seg), i32_to_gpu(a_rows)
+    p1 = sq.prepare(bf16_to_gpu(wl["x"]), None, 2, 4)
+    gu = sq.linear_grouped(p1, w_gu, seg_g, rows_g)
+    h = sq.silu_mul(gu)
+    p2 = sq.prepare(h, None, 2, 4)
+    y = sq.linear_grouped(p2, w_dn, seg_g, None)
+    torch.cuda.synchronize()
+    # sampled pairs across experts, including the first and last pair of some segments
+    rng = np.random.default_rng(12)
+    pairs = np.unique(np.concatenate([seg[:-1][seg[:-1] < P][::9], rng.choice(P, 40, replace=False), [P - 1]]))
+    e_of = np.searchsorted(seg, pairs, side="right") - 1
+    toks = a_rows[pairs]
+    o1 = prepare_ref(wl["x"][toks], None, 2, 4)
+    assert_prepare_equal(p1, o1, rows=toks)
+    gu_np, h_np = to_np(gu), to_np(h)
+    cols = np.concatenate([_sample(I, 48, 1), I + _sample(I, 48, 2)])
+    dcols = _sample(H, 96, 3)
+    o2 = prepare_ref(h_np[pairs], None, 2, 4)
+    assert_prepare_equal(p2, o2, rows=pairs)
+    y_np = to_np(y)
+    for idx, (pp, e) in enumerate(zip(pairs, e_of)):
+        wc, ws = quantize_weight_ref(wl["w_gu"][e][cols])
+        yr, b = linear_ref(o1["bb_codes"][idx:idx + 1], o1["bb_scales"][idx:idx + 1], o1["res_codes"][idx:idx + 1],
+                           o1["res_scales"][idx:idx + 1], wc, ws)
+        assert_y_close(gu_np[pp:pp + 1, cols], yr, b)
+        wc, ws = quantize_weight_ref(wl["w_down"][e][dcols])
+        yr, b = linear_ref(o2["bb_codes"][idx:idx + 1], o2["bb_scales"][idx:idx + 1], o2["res_codes"][idx:idx + 1],
+                           o2["res_scales"][idx:idx + 1], wc, ws)
+        assert_y_close(y_np[pp:pp + 1, dcols], yr, b)
+    want_h = silu_mul_ref(gu_np[pairs], I)
+    assert_bf16_close(h_np[pairs], want_h)

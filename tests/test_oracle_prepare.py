@@ -7,7 +7,7 @@ import pytest
 
 from oracle import (absorb_gamma, mxfp4_dequantize, mxfp4_quantize, pack_nibbles,
                     prepare_ref, unpack_mask, unpack_nibbles)
-from synth import bf16_round, bf16_to_f32, workload_down_silu, workload_linear
+from synth import adversarial_rows, bf16_round, bf16_to_f32, workload_down_silu, workload_linear
 
 
 def test_hand_worked_2of4_block():
@@ -32,26 +32,6 @@ def test_hand_worked_2of4_block():
     assert out["res_codes"].tolist() == [[0x06, 0x04, 0x22, 0x22, 0, 0, 0xDA, 0x02] + [0] * 8]
 
 
-def _adversarial_rows(K, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = []
-    rows.append(np.zeros(K))
-    rows.append(np.where(np.arange(K) % 2, -0.0, 0.0))
-    rows.append(np.full(K, 1.5))
-    rows.append(np.full(K, -2.0 ** -130))  # bf16 subnormal
-    rows.append(rng.choice([1.0, -1.0, 2.0, 0.0], size=K))
-    rows.append(rng.standard_normal(K) * 2.0 ** -128)  # mixes normals and subnormals
-    big = rng.standard_normal(K)
-    big[::13] *= 1e30
-    rows.append(big)
-    rows.append(rng.standard_normal(K) * 1e37)
-    rows.append(np.ldexp(1.0, rng.integers(-133, 127, K)) * rng.choice([-1, 1], K))
-    sat = rng.standard_normal(K)
-    sat[::32] = 7.0  # a value of 7 * 2**e lands between 6 and 8
-    rows.append(sat)
-    return np.array(rows, dtype=np.float32)
-
-
 CASES = [
     ("2of4", 2, 4),
     ("8of16", 8, 16),
@@ -62,7 +42,7 @@ def _inputs(K, seed):
     rng = np.random.default_rng(seed)
     base = (rng.standard_normal((20, K)) * rng.lognormal(0, 1, (20, 1))).astype(np.float32)
     base[:, rng.choice(K, 3, replace=False)] *= 50
-    return bf16_round(np.concatenate([base, _adversarial_rows(K, seed)]))
+    return bf16_round(np.concatenate([base, adversarial_rows(K, seed)]))
 
 
 @pytest.mark.parametrize("name,n,m", CASES)

@@ -148,8 +148,9 @@ def linear_grouped(prep: Prepared, w: MXFP4, seg_offsets, a_rows=None, out=None)
     if out is None:
         out = torch.empty((P, O), dtype=torch.float32, device=w.codes.device)
     st = _lib.call("sharq_linear_grouped", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
-                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), _ptr(a_rows), seg_offsets.data_ptr(), E,
-                   w.codes.data_ptr(), w.scales.data_ptr(), P, O, K, out.data_ptr(), _stream(out.device))
+                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), prep.bb_codes.shape[0], _ptr(a_rows),
+                   seg_offsets.data_ptr(), E, w.codes.data_ptr(), w.scales.data_ptr(), P, O, K, out.data_ptr(),
+                   _stream(out.device))
     _lib.check("sharq_linear_grouped", st)
     return out
 

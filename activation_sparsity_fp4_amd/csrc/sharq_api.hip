@@ -80,10 +80,12 @@ int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_
 }
 
 int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
-                         const uint8_t* res_scales, const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,
-                         const uint8_t* w_codes, const uint8_t* w_scales, int64_t P, int64_t O, int64_t K, float* y,
-                         hipStream_t stream) {
-  if (E < 1 || P < 0 || O < 0 || K <= 0 || K % 32 != 0) return SHARQ_EINVAL;
+                         const uint8_t* res_scales, int64_t T_src, const int32_t* a_rows, const int32_t* seg_offsets,
+                         int32_t E, const uint8_t* w_codes, const uint8_t* w_scales, int64_t P, int64_t O, int64_t K,
+                         float* y, hipStream_t stream) {
+  if (E < 1 || P < 0 || O < 0 || K <= 0 || K % 32 != 0 || T_src < 0) return SHARQ_EINVAL;
+  if (!a_rows && T_src < P) return SHARQ_EINVAL;
+  if (T_src >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
   if (P >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31) ||
       (P + 127) / 128 + E > 65535)
     return SHARQ_EINVAL;
@@ -95,7 +97,7 @@ int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales, cons
       (a_rows && !aligned16(a_rows)))
     return SHARQ_EALIGN;
   return hip_status(sharq::launch_linear_grouped(bb_codes, bb_scales, res_codes, res_scales, a_rows, seg_offsets,
-                                                 E, w_codes, w_scales, P, O, K, y, stream));
+                                                 E, w_codes, w_scales, P, O, K, y, T_src, stream));
 }
 
 int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {

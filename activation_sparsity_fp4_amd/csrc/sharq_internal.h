@@ -21,7 +21,7 @@ hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scal
                                  const uint8_t* res_codes, const uint8_t* res_scales,
                                  const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,
                                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t P, int64_t O,
-                                 int64_t K, float* y, hipStream_t stream);
+                                 int64_t K, float* y, int64_t a_rows_total, hipStream_t stream);
 
 hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream);
 

@@ -119,14 +119,18 @@ SHARQ_API int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales,
  * Output row p (0 <= p < P) belongs to the expert e with
  * seg_offsets[e] <= p < seg_offsets[e+1]; it reads activation row a_rows[p]
  * (or row p when a_rows is NULL) and expert e's weight.
+ *  bb_codes/res_codes u8 [T_src][K/2], bb_scales/res_scales u8 [T_src][K/32]
+ *              the prepared activation rows (T_src >= P when a_rows is NULL).
  *  a_rows      i32 [P] device, each in [0, T_src), or NULL.
  *  seg_offsets i32 [E+1] device, non-decreasing, [0] = 0, [E] = P.
  *  w_codes u8 [E][O][K/2], w_scales u8 [E][O][K/32]; y fp32 [P][O].
- * Segment contents are read on the device; their validity is a precondition.
+ * Segment and gather contents are read on the device; their validity is a
+ * precondition (a gathered row outside [0, T_src) reads as zeros).
  */
 SHARQ_API int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales,
                          const uint8_t* res_codes, const uint8_t* res_scales,
-                         const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,
+                         int64_t T_src, const int32_t* a_rows,
+                         const int32_t* seg_offsets, int32_t E,
                          const uint8_t* w_codes, const uint8_t* w_scales,
                          int64_t P, int64_t O, int64_t K, float* y,
                          hipStream_t stream);

@@ -94,8 +94,8 @@ def test_linear_validation():
     assert lin(y=G + 4) == _lib.SHARQ_EALIGN
 
 
-def grp(P=16, O=8, K=64, E=2, a_rows=A, seg=B, **kw):
-    return _lib.call("sharq_linear_grouped", C, D, E_, F, a_rows, seg, E, G, G + 4096, P, O, K, 0x90000, 0)
+def grp(P=16, O=8, K=64, E=2, a_rows=A, seg=B, T_src=16, **kw):
+    return _lib.call("sharq_linear_grouped", C, D, E_, F, T_src, a_rows, seg, E, G, G + 4096, P, O, K, 0x90000, 0)
 
 
 def test_grouped_validation():
@@ -105,6 +105,8 @@ def test_grouped_validation():
     assert grp(K=40) == _lib.SHARQ_EINVAL
     assert grp(a_rows=A + 4) == _lib.SHARQ_EALIGN
     assert grp(P=1 << 24, E=1) == _lib.SHARQ_EINVAL  # grid bound
+    assert grp(a_rows=0, T_src=8) == _lib.SHARQ_EINVAL  # identity rows need T_src >= P
+    assert grp(T_src=-1) == _lib.SHARQ_EINVAL
 
 
 def test_silu_and_quantize_validation():

@@ -30,17 +30,27 @@ __all__ = [
 
 
 class Prepared(NamedTuple):
-    """Outputs of the prepare operator (all uint8 device tensors)."""
+    """Outputs of the prepare operator (all uint8 device tensors).
+
+    Scales are stage-major: [ceil(K/128), T, 4], byte (k // 32) % 4 of entry
+    [k // 128, t]; bytes past the last block of a row are zero."""
     bb_codes: "object"    # [T, K/2]
-    bb_scales: "object"   # [T, K/32]
+    bb_scales: "object"   # [G, T, 4], G = ceil(K/128)
     res_codes: "object"   # [T, K/2]
-    res_scales: "object"  # [T, K/32]
+    res_scales: "object"  # [G, T, 4]
     mask: "object"        # [T, K/8] or None
 
 
 class MXFP4(NamedTuple):
-    codes: "object"   # uint8 [..., K/2]
-    scales: "object"  # uint8 [..., K/32]
+    """A block-scaled FP4 tensor: codes [R, K/2] with stage-major scales
+    [G, R, 4]; for expert weights codes [E, O, K/2] and scales [E, G, O, 4]."""
+    codes: "object"
+    scales: "object"
+
+
+def stages(K: int) -> int:
+    """Number of 128-entry K stages (the leading dimension of a scale tensor)."""
+    return (K + 127) // 128
 
 
 def _torch():
@@ -81,8 +91,9 @@ def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: 
         gamma = gamma.contiguous()
     if out is None:
         kw = dict(dtype=torch.uint8, device=x.device)
-        out = Prepared(torch.empty((T, K // 2), **kw), torch.empty((T, K // 32), **kw),
-                       torch.empty((T, K // 2), **kw), torch.empty((T, K // 32), **kw),
+        G = stages(K)
+        out = Prepared(torch.empty((T, K // 2), **kw), torch.empty((G, T, 4), **kw),
+                       torch.empty((T, K // 2), **kw), torch.empty((G, T, 4), **kw),
                        torch.empty((T, K // 8), **kw) if with_mask else None)
     st = _lib.call("sharq_prepare", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), n, m,
                    out.bb_codes.data_ptr(), out.bb_scales.data_ptr(), out.res_codes.data_ptr(),
@@ -92,15 +103,25 @@ def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: 
 
 
 def quantize_mxfp4(x, out: Optional[MXFP4] = None) -> MXFP4:
-    """Plain MXFP4 along the last axis of a bf16 [R, K] tensor (e.g. a weight [O, K])."""
+    """Plain MXFP4 along the last axis of a bf16 [R, K] tensor (e.g. a weight
+    [O, K]), or of a stack of expert weights [E, O, K] (one call per expert,
+    so each expert owns a contiguous [G, O, 4] scale block)."""
     torch = _torch()
+    if x.dim() == 3:
+        E, R, K = x.shape
+        if out is None:
+            out = MXFP4(torch.empty((E, R, K // 2), dtype=torch.uint8, device=x.device),
+                        torch.empty((E, stages(K), R, 4), dtype=torch.uint8, device=x.device))
+        for e in range(E):
+            quantize_mxfp4(x[e], MXFP4(out.codes[e], out.scales[e]))
+        return out
     _need(x, torch.bfloat16, "x", 2)
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous along K")
     R, K = x.shape
     if out is None:
         out = MXFP4(torch.empty((R, K // 2), dtype=torch.uint8, device=x.device),
-                    torch.empty((R, K // 32), dtype=torch.uint8, device=x.device))
+                    torch.empty((stages(K), R, 4), dtype=torch.uint8, device=x.device))
     st = _lib.call("sharq_quantize_mxfp4", x.data_ptr(), R, K, x.stride(0), out.codes.data_ptr(),
                    out.scales.data_ptr(), _stream(x.device))
     _lib.check("sharq_quantize_mxfp4", st)
@@ -110,10 +131,12 @@ def quantize_mxfp4(x, out: Optional[MXFP4] = None) -> MXFP4:
 def linear(prep: Prepared, w: MXFP4, out=None):
     """Two-path FP4 GEMM: Y = deq(backbone) W^T + deq(residual) W^T, fp32 [T, O]."""
     torch = _torch()
-    for name in ("bb_codes", "bb_scales", "res_codes", "res_scales"):
+    for name in ("bb_codes", "res_codes"):
         _need(getattr(prep, name), torch.uint8, name, 2)
+    for name in ("bb_scales", "res_scales"):
+        _need(getattr(prep, name), torch.uint8, name, 3)
     _need(w.codes, torch.uint8, "w.codes", 2)
-    _need(w.scales, torch.uint8, "w.scales", 2)
+    _need(w.scales, torch.uint8, "w.scales", 3)
     T, Kh = prep.bb_codes.shape
     O = w.codes.shape[0]
     K = 2 * Kh
@@ -134,7 +157,7 @@ def linear_grouped(prep: Prepared, w: MXFP4, seg_offsets, a_rows=None, out=None)
     seg_offsets int32 [E+1]; a_rows int32 [P] (source row of each sorted pair) or None."""
     torch = _torch()
     _need(w.codes, torch.uint8, "w.codes", 3)
-    _need(w.scales, torch.uint8, "w.scales", 3)
+    _need(w.scales, torch.uint8, "w.scales", 4)
     _need(seg_offsets, torch.int32, "seg_offsets", 1)
     E, O, Kh = w.codes.shape
     K = 2 * Kh

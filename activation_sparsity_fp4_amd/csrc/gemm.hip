@@ -29,6 +29,10 @@
 // c ^ ((r >> 2) & 3), which keeps the rows read by one MFMA fragment on
 // distinct banks of the 64-bank LDS.
 //
+// Scales are stored stage-major ([K/128][rows][4], see sharq_device.h): one
+// stage of a 128-row tile is a single contiguous 512-byte run, so the scale
+// loads cost a few L2 requests per stage rather than one per row.
+//
 // MFMA operand layouts (32x32x64, FP4): lane l holds row (l % 32) and the 32
 // consecutive K entries of block (l / 32) of the 64-entry K slice, low nibble
 // first, in 4 VGPRs; its scale byte covers exactly those 32 entries. The
@@ -177,6 +181,7 @@ struct RingLoader {
   uint32_t s_off[2];   // scale-row byte offsets for this wave's two scale instructions
   int wave;            // wave-uniform
   int nsteps;
+  uint32_t a_stage_bytes, w_stage_bytes;  // scale bytes of one stage: 4 per row
 
   // Issue the 10 loads of stage s (K entries [128 s, 128 s + 128)) into `st`.
   // Past the last stage every offset is moved out of range: the loads keep
@@ -196,12 +201,13 @@ struct RingLoader {
       const int chunk = wave + 4 * j;  // 1 KB chunk inside the 16 KB W tile
       buffer_to_lds16(w_codes, w_off[j] + kc, base + kOffW + 1024 * chunk);
     }
-    const uint32_t ks = live ? (uint32_t)s * 4 : kOOB;
+    const uint32_t ksa = live ? (uint32_t)s * a_stage_bytes : kOOB;
+    const uint32_t ksw = live ? (uint32_t)s * w_stage_bytes : kOOB;
     // scale rows: waves 0,1 -> backbone rows 64w..; waves 2,3 -> residual rows; then W rows 64w..
     const i32x4 ars = wave < 2 ? a_scales[0] : a_scales[1];
     const uint32_t aoff = (wave < 2 ? kOffSAs : kOffSAr) + 256 * (wave & 1);
-    buffer_to_lds4(ars, s_off[0] + ks, base + aoff);
-    buffer_to_lds4(w_scales, s_off[1] + ks, base + kOffSW + 256 * wave);
+    buffer_to_lds4(ars, s_off[0] + ksa, base + aoff);
+    buffer_to_lds4(w_scales, s_off[1] + ksw, base + kOffSW + 256 * wave);
   }
 };
 
@@ -323,6 +329,8 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   ld.a_scales[1] = make_rsrc(op.a_scales[1], op.a_rows_total * kblocks);
   ld.w_codes = make_rsrc(op.w_codes, op.O * kbytes);
   ld.w_scales = make_rsrc(op.w_scales, op.O * kblocks);
+  ld.a_stage_bytes = (uint32_t)(op.a_rows_total * 4);
+  ld.w_stage_bytes = (uint32_t)(op.O * 4);
   // The LDS chunk position a lane fills is fixed (lane * 16 inside its 1 KB
   // chunk); pick the global 16-byte chunk that belongs there after the swizzle.
 #pragma unroll
@@ -341,9 +349,9 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   }
   {
     const int64_t src = tr.src(64 * (wave & 1) + lane);
-    ld.s_off[0] = src >= 0 ? (uint32_t)(src * kblocks) : kOOB;
+    ld.s_off[0] = src >= 0 ? (uint32_t)(src * 4) : kOOB;
     const int64_t o = n0 + 64 * wave + lane;
-    ld.s_off[1] = o < op.O ? (uint32_t)(o * kblocks) : kOOB;
+    ld.s_off[1] = o < op.O ? (uint32_t)(o * 4) : kOOB;
   }
 
   const int nsteps = op.nsteps;
@@ -377,16 +385,14 @@ struct Prefetch {
   uint32_t sw;    // scale dword of one W row
 };
 
-// 4 scale bytes of one row for K entries [128 s, 128 s + 128); bytes past the
-// end of K read as 127 (scale 1.0; their codes are zero).
-__device__ __forceinline__ uint32_t load_scales4(const uint8_t* row, int64_t s, int64_t kblocks) {
-  uint32_t v = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t b = 4 * s + i;
-    const uint32_t byte = b < kblocks ? row[b] : 127u;
-    v |= byte << (8 * i);
-  }
+// The scale dword of (stage s, row) in the stage-major layout; bytes of a
+// last, partial stage past the row's blocks are masked to zero (their codes
+// are zero too).
+__device__ __forceinline__ uint32_t load_scales4(const uint8_t* scales, int64_t row, int64_t rows, int64_t s,
+                                                 int64_t kblocks) {
+  uint32_t v = *reinterpret_cast<const uint32_t*>(scales + s * rows * 4 + row * 4);
+  const int64_t valid = kblocks - 4 * s;
+  if (valid < 4) v &= (1u << (8 * valid)) - 1u;
   return v;
 }
 
@@ -417,8 +423,8 @@ __device__ __forceinline__ void load_stage_regs(Prefetch& pf, const Operands& op
   }
   const int64_t kblocks = op.K >> 5;
   const uint8_t* sbase = (tid >> 7) ? op.a_scales[1] : op.a_scales[0];
-  pf.sa = a_src_scale >= 0 ? load_scales4(sbase + a_src_scale * kblocks, s, kblocks) : 0x7F7F7F7Fu;
-  pf.sw = w_row_scale >= 0 ? load_scales4(op.w_scales + w_row_scale * kblocks, s, kblocks) : 0x7F7F7F7Fu;
+  pf.sa = a_src_scale >= 0 ? load_scales4(sbase, a_src_scale, op.a_rows_total, s, kblocks) : 0x7F7F7F7Fu;
+  pf.sw = w_row_scale >= 0 ? load_scales4(op.w_scales, w_row_scale, op.O, s, kblocks) : 0x7F7F7F7Fu;
 }
 
 __device__ __forceinline__ void store_stage_regs(const Prefetch& pf, uint8_t* st, int tid) {
@@ -582,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void linear_grouped_kernel(
   tr.gather = a_rows;
   const int64_t n0 = (int64_t)blockIdx.x * kBN;
   op.w_codes = w_codes_all + (int64_t)e * op.O * (op.K >> 1);
-  op.w_scales = w_scales_all + (int64_t)e * op.O * (op.K >> 5);
+  op.w_scales = w_scales_all + (int64_t)e * op.O * 4 * op.nsteps;  // [E][K/128 stages][O][4]
   v16f acc[2][4];
   zero_acc(acc);
   if constexpr (kRingPath)

@@ -11,9 +11,8 @@
 // block reduction (amax, scale) and every N:M group (4 or 16 entries, both
 // dividing 32) stays inside the lane's registers and no cross-lane traffic is
 // needed. A lane reads 64 contiguous bytes of bf16 (four 16-byte loads) and
-// writes 16 + 16 bytes of codes, two scale bytes and a 32-bit mask word; lanes
-// of a wave own consecutive blocks of a row, so all accesses are contiguous
-// across the wave. The kernel is HBM-bound: 2 bytes read and 1.1875 bytes
+// writes 16 + 16 bytes of codes, two scale bytes and a 32-bit mask word (see
+// block_of_lane for how lanes map to blocks). The kernel is HBM-bound: 2 bytes read and 1.1875 bytes
 // written per element.
 //
 // Selection: magnitudes are compared as integer bit patterns. When the low
@@ -103,17 +102,49 @@ __device__ __forceinline__ uint32_t select_exact(const float (&x)[32]) {
   return mask;
 }
 
+// Lane -> (row, block) map shared by the prepare and quantise kernels. A wave
+// owns a band of 16 rows and one 128-entry K stage (4 blocks): lane l takes
+// row 16 * band + l / 4 and block 4 * stage + l % 4. Its 64 stage-major scale
+// bytes are then one contiguous run, each row's input is read in 256-byte
+// runs and its codes written in 64-byte runs; consecutive waves walk the
+// stages of a band, so the two halves of a code cache line are written by
+// neighbouring waves.
+struct BlockOfLane {
+  uint32_t t, b;
+  bool row_ok, block_ok;
+};
+
+__device__ __forceinline__ BlockOfLane block_of_lane(uint32_t stages, uint32_t blocks_per_row, uint32_t rows) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t wave = gid >> 6, lane = gid & 63;
+  const uint32_t band = wave / stages;
+  const uint32_t g = wave - band * stages;
+  BlockOfLane r;
+  r.t = band * 16 + (lane >> 2);
+  r.b = g * 4 + (lane & 3);
+  r.row_ok = r.t < rows;
+  r.block_ok = r.row_ok && r.b < blocks_per_row;
+  return r;
+}
+
 template <int N, int M, bool kGamma>
 __global__ __launch_bounds__(256) void prepare_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma,
-    uint32_t blocks_per_row, uint32_t total_blocks,
+    uint32_t blocks_per_row, uint32_t stages, uint32_t rows,
     uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_scales,
     uint8_t* __restrict__ res_codes, uint8_t* __restrict__ res_scales,
     uint8_t* __restrict__ mask_out) {
-  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= total_blocks) return;
-  const uint32_t t = gid / blocks_per_row;
-  const uint32_t b = gid - t * blocks_per_row;
+  const BlockOfLane lb = block_of_lane(stages, blocks_per_row, rows);
+  if (!lb.block_ok) {
+    // the unused bytes of a last, partial stage are zero
+    if (lb.row_ok) {
+      bb_scales[scale_index(lb.t, lb.b, rows)] = 0;
+      res_scales[scale_index(lb.t, lb.b, rows)] = 0;
+    }
+    return;
+  }
+  const uint32_t t = lb.t, b = lb.b;
+  const uint32_t gid = t * blocks_per_row + b;  // row-major block index (mask words)
 
   // load 32 bf16 (64 B) and widen to fp32
   const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * ldx + (int64_t)b * kBlock);
@@ -179,20 +210,22 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   const int64_t row_codes = (int64_t)blocks_per_row * (kBlock / 2);
   reinterpret_cast<uint4*>(bb_codes + (int64_t)t * row_codes)[b] = c_bb;
   reinterpret_cast<uint4*>(res_codes + (int64_t)t * row_codes)[b] = c_rs;
-  bb_scales[gid] = (uint8_t)e_bb;
-  res_scales[gid] = (uint8_t)e_rs;
+  bb_scales[scale_index(t, b, rows)] = (uint8_t)e_bb;
+  res_scales[scale_index(t, b, rows)] = (uint8_t)e_rs;
   if (mask_out) reinterpret_cast<uint32_t*>(mask_out)[gid] = keep;
 }
 
 // Plain MXFP4 coding of bf16 rows (the weight quantiser): same element and
 // scale rules, no mask and no residual.
 __global__ __launch_bounds__(256) void quantize_kernel(
-    const uint16_t* __restrict__ x, int64_t ldx, uint32_t blocks_per_row, uint32_t total_blocks,
+    const uint16_t* __restrict__ x, int64_t ldx, uint32_t blocks_per_row, uint32_t stages, uint32_t rows,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= total_blocks) return;
-  const uint32_t t = gid / blocks_per_row;
-  const uint32_t b = gid - t * blocks_per_row;
+  const BlockOfLane lb = block_of_lane(stages, blocks_per_row, rows);
+  if (!lb.block_ok) {
+    if (lb.row_ok) scales[scale_index(lb.t, lb.b, rows)] = 0;
+    return;
+  }
+  const uint32_t t = lb.t, b = lb.b;
   const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * ldx + (int64_t)b * kBlock);
   float xv[32];
 #pragma unroll
@@ -209,24 +242,28 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   const uint4 c = quantize32(xv, scale_from_e8m0(e));
   const int64_t row_codes = (int64_t)blocks_per_row * (kBlock / 2);
   reinterpret_cast<uint4*>(codes + (int64_t)t * row_codes)[b] = c;
-  scales[gid] = (uint8_t)e;
+  scales[scale_index(t, b, rows)] = (uint8_t)e;
 }
 
-static inline unsigned grid_for(uint32_t total, unsigned threads) {
-  return (total + threads - 1) / threads;
+// Threads for the lane map of block_of_lane: one wave per (16-row band, stage).
+static inline uint64_t lanes_for(int64_t T, int64_t K) {
+  const uint64_t bands = (uint64_t)((T + 15) / 16);
+  const uint64_t stages = (uint64_t)((K + 127) / 128);
+  return bands * stages * 64;
 }
 
 hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma,
                           int n, int m, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
                           uint8_t* res_scales, uint8_t* mask, hipStream_t stream) {
   const uint32_t bpr = (uint32_t)(K / kBlock);
-  const uint32_t total = (uint32_t)(T * bpr);
+  const uint32_t stages = (uint32_t)((K + 127) / 128);
+  const uint64_t lanes = lanes_for(T, K);
   // small problems: one wave per workgroup so that more CUs take part
-  const unsigned threads = total >= (1u << 18) ? 256 : 64;
-  const dim3 grid(grid_for(total, threads)), block(threads);
+  const unsigned threads = lanes >= (1u << 18) ? 256 : 64;
+  const dim3 grid((unsigned)((lanes + threads - 1) / threads)), block(threads);
 #define SHARQ_PREP(NN, MM, GG)                                                              \
   hipLaunchKernelGGL((prepare_kernel<NN, MM, GG>), grid, block, 0, stream, x, ldx, gamma,   \
-                     bpr, total, bb_codes, bb_scales, res_codes, res_scales, mask)
+                     bpr, stages, (uint32_t)T, bb_codes, bb_scales, res_codes, res_scales, mask)
   if (n == 2 && m == 4) {
     if (gamma) SHARQ_PREP(2, 4, true); else SHARQ_PREP(2, 4, false);
   } else {
@@ -239,10 +276,11 @@ hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, 
 hipError_t launch_quantize(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream) {
   const uint32_t bpr = (uint32_t)(K / kBlock);
-  const uint32_t total = (uint32_t)(T * bpr);
-  const unsigned threads = total >= (1u << 18) ? 256 : 64;
-  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(total, threads)), dim3(threads), 0, stream, x, ldx,
-                     bpr, total, codes, scales);
+  const uint32_t stages = (uint32_t)((K + 127) / 128);
+  const uint64_t lanes = lanes_for(T, K);
+  const unsigned threads = lanes >= (1u << 18) ? 256 : 64;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)((lanes + threads - 1) / threads)), dim3(threads), 0, stream,
+                     x, ldx, bpr, stages, (uint32_t)T, codes, scales);
   return hipGetLastError();
 }
 

@@ -65,6 +65,15 @@ __device__ __forceinline__ void dequantize32(uint4 c, float scale, float (&q)[32
   }
 }
 
+// Scale layout shared by every kernel: the E8M0 bytes of a [rows x K] MXFP4
+// tensor are grouped by 128-entry K stage, [ceil(K/128)][rows][4]: byte
+// (k / 32) % 4 of the dword for (stage k / 128, row). One GEMM stage of a row
+// tile then reads one contiguous run of dwords instead of one scattered byte
+// run per row. Bytes of a last, partial stage past K / 32 blocks are zero.
+__device__ __forceinline__ int64_t scale_index(int64_t row, uint32_t block, int64_t rows) {
+  return (int64_t)(block >> 2) * rows * 4 + row * 4 + (block & 3);
+}
+
 // Largest |v| of 32 floats as a bit pattern (sign cleared). Integer max on
 // the magnitude bits orders non-negative floats exactly.
 __device__ __forceinline__ uint32_t amax_bits32(const float (&v)[32]) {

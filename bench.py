@@ -170,10 +170,8 @@ def build_workload(name, torch, sq):
         P = len(wl["a_rows"])
         tokens = wl["x"].shape[0]
         x = _to_gpu_bf16(torch, wl["x"])
-        wg = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"].reshape(E * 2 * I, H)))
-        wd = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"].reshape(E * H, I)))
-        w_gu = sq.MXFP4(wg.codes.view(E, 2 * I, H // 2), wg.scales.view(E, 2 * I, H // 32))
-        w_dn = sq.MXFP4(wd.codes.view(E, H, I // 2), wd.scales.view(E, H, I // 32))
+        w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"].reshape(E * 2 * I, H)).view(E, 2 * I, H))
+        w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"].reshape(E * H, I)).view(E, H, I))
         seg = torch.from_numpy(wl["seg_offsets"]).cuda()
         rows = torch.from_numpy(wl["a_rows"]).cuda()
         buf = {"p1": sq.prepare(x, None, 2, 4)}

@@ -40,11 +40,45 @@ def to_np(t):
     return t.numpy()
 
 
+def stage_major(s_rows):
+    """Row-major scales [R, K/32] (the oracle's form) -> the library's stage-major
+    [ceil(K/128), R, 4] layout, zero past the last block. Pure data movement."""
+    s_rows = np.asarray(s_rows, dtype=np.uint8)
+    R, kb = s_rows.shape
+    G = (kb + 3) // 4
+    pad = np.zeros((R, 4 * G), dtype=np.uint8)
+    pad[:, :kb] = s_rows
+    return np.ascontiguousarray(pad.reshape(R, G, 4).transpose(1, 0, 2))
+
+
+def row_major(s_stage, kblocks):
+    """Stage-major [G, R, 4] -> row-major [R, K/32]; checks the padding bytes are zero."""
+    s_stage = np.asarray(s_stage, dtype=np.uint8)
+    G, R, _ = s_stage.shape
+    flat = s_stage.transpose(1, 0, 2).reshape(R, 4 * G)
+    assert not flat[:, kblocks:].any(), "scale padding bytes must be zero"
+    return flat[:, :kblocks]
+
+
+def w_to_gpu(wc, ws):
+    """Upload an oracle-quantised weight (codes [O, K/2] or [E, O, K/2], row-major scales)."""
+    import activation_sparsity_fp4_amd as sq
+    ws = np.asarray(ws)
+    if ws.ndim == 3:
+        return sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(np.stack([stage_major(x) for x in ws])))
+    return sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(stage_major(ws)))
+
+
+def w_scales_rows(wq_scales, kblocks):
+    """GPU weight scales [G, O, 4] -> row-major [O, K/32]."""
+    return row_major(to_np(wq_scales), kblocks)
+
+
 def oracle_prepared(out):
     """Upload an oracle prepare result as the GPU's Prepared tuple."""
     import activation_sparsity_fp4_amd as sq
-    return sq.Prepared(u8_to_gpu(out["bb_codes"]), u8_to_gpu(out["bb_scales"]), u8_to_gpu(out["res_codes"]),
-                       u8_to_gpu(out["res_scales"]), None)
+    return sq.Prepared(u8_to_gpu(out["bb_codes"]), u8_to_gpu(stage_major(out["bb_scales"])),
+                       u8_to_gpu(out["res_codes"]), u8_to_gpu(stage_major(out["res_scales"])), None)
 
 
 def assert_prepare_equal(got, want, rows=None):
@@ -54,6 +88,8 @@ def assert_prepare_equal(got, want, rows=None):
         if g is None:
             continue
         g = to_np(g)
+        if name.endswith("scales"):
+            g = row_major(g, want[name].shape[1])
         if rows is not None:
             g = g[rows]
         w = want[name]

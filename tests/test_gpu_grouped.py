@@ -12,7 +12,7 @@ import pytest
 from oracle import (linear_grouped_ref, linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref)
 from synth import bf16_round, bf16_to_f32, moe_routing, workload_llama8b_mlp, workload_qwen3_moe
 from gpu_util import (assert_bf16_close, assert_prepare_equal, assert_y_close, bf16_to_gpu, f32_to_gpu,
-                      i32_to_gpu, oracle_prepared, to_np, u8_to_gpu)
+                      i32_to_gpu, oracle_prepared, to_np, u8_to_gpu, w_to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def test_grouped_small_with_empty_and_single_row_experts(sq, use_rows):
         a_rows = None
         P = tokens
         seg = np.array([0, 1, 1, 130, 131, 260, 299, P], np.int32)
-    y = sq.linear_grouped(oracle_prepared(p), sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws)), i32_to_gpu(seg),
+    y = sq.linear_grouped(oracle_prepared(p), w_to_gpu(wc, ws), i32_to_gpu(seg),
                           None if a_rows is None else i32_to_gpu(a_rows))
     y_ref, bound = linear_grouped_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], a_rows, seg,
                                       wc, ws)
@@ -117,10 +117,8 @@ def test_qwen3_moe_layer_chain(sq):
     E, I, H = wl["experts"], wl["inter"], wl["hidden"]
     a_rows, seg = wl["a_rows"], wl["seg_offsets"]
     P = len(a_rows)
-    w_gu = sq.quantize_mxfp4(bf16_to_gpu(wl["w_gu"].reshape(E * 2 * I, H)))
-    w_dn = sq.quantize_mxfp4(bf16_to_gpu(wl["w_down"].reshape(E * H, I)))
-    w_gu = sq.MXFP4(w_gu.codes.view(E, 2 * I, H // 2), w_gu.scales.view(E, 2 * I, H // 32))
-    w_dn = sq.MXFP4(w_dn.codes.view(E, H, I // 2), w_dn.scales.view(E, H, I // 32))
+    w_gu = sq.quantize_mxfp4(bf16_to_gpu(wl["w_gu"].reshape(E * 2 * I, H)).view(E, 2 * I, H))
+    w_dn = sq.quantize_mxfp4(bf16_to_gpu(wl["w_down"].reshape(E * H, I)).view(E, H, I))
     seg_g, rows_g = i32_to_gpu(seg), i32_to_gpu(a_rows)
     p1 = sq.prepare(bf16_to_gpu(wl["x"]), None, 2, 4)
     gu = sq.linear_grouped(p1, w_gu, seg_g, rows_g)

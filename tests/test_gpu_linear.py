@@ -12,7 +12,8 @@ import pytest
 
 from oracle import linear_ref, prepare_ref, quantize_weight_ref
 from synth import bf16_round, workload_down_silu, workload_linear, workload_llama8b_mlp
-from gpu_util import (assert_prepare_equal, assert_y_close, bf16_to_gpu, oracle_prepared, to_np, u8_to_gpu)
+from gpu_util import (assert_prepare_equal, assert_y_close, bf16_to_gpu, oracle_prepared, to_np, u8_to_gpu,
+                      w_scales_rows, w_to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +42,7 @@ def _random_problem(T, O, K, seed, n=2, m=4):
 def test_linear_small(sq, T, O, K):
     print(f"linear T={T} O={O} K={K}", flush=True)
     p, wc, ws = _random_problem(T, O, K, seed=T * 7 + O)
-    y = sq.linear(oracle_prepared(p), sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws)))
+    y = sq.linear(oracle_prepared(p), w_to_gpu(wc, ws))
     y_ref, bound = linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
     assert_y_close(to_np(y), y_ref, bound)
 
@@ -52,14 +53,17 @@ def test_linear_strided_output_and_zero_rows(sq):
     T, O, K = 70, 96, 256
     p, wc, ws = _random_problem(T, O, K, seed=4)
     out = torch.full((T, O + 40), 7.0, dtype=torch.float32, device="cuda")[:, :O]
-    sq.linear(oracle_prepared(p), sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws)), out=out)
+    sq.linear(oracle_prepared(p), w_to_gpu(wc, ws), out=out)
     y_ref, bound = linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
     assert_y_close(to_np(out), y_ref, bound)
     full = to_np(out.as_strided((T, O + 40), (O + 40, 1)))
     assert np.all(full[:, O:] == 7.0)  # padding columns untouched
-    e = sq.Prepared(*(torch.empty((0, s), dtype=torch.uint8, device="cuda") for s in (K // 2, K // 32, K // 2, K // 32)),
-                    None)
-    y0 = sq.linear(e, sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws)))
+    G = sq.stages(K)
+    e = sq.Prepared(torch.empty((0, K // 2), dtype=torch.uint8, device="cuda"),
+                    torch.empty((G, 0, 4), dtype=torch.uint8, device="cuda"),
+                    torch.empty((0, K // 2), dtype=torch.uint8, device="cuda"),
+                    torch.empty((G, 0, 4), dtype=torch.uint8, device="cuda"), None)
+    y0 = sq.linear(e, w_to_gpu(wc, ws))
     assert y0.shape == (0, O)
 
 
@@ -71,7 +75,7 @@ def test_linear_residual_only_and_backbone_only(sq):
     for zero in ("bb_codes", "res_codes"):
         q = dict(p)
         q[zero] = np.zeros_like(p[zero])
-        y = sq.linear(oracle_prepared(q), sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws)))
+        y = sq.linear(oracle_prepared(q), w_to_gpu(wc, ws))
         y_ref, bound = linear_ref(q["bb_codes"], q["bb_scales"], q["res_codes"], q["res_scales"], wc, ws)
         assert_y_close(to_np(y), y_ref, bound)
 
@@ -79,8 +83,8 @@ def test_linear_residual_only_and_backbone_only(sq):
 def test_linear_deterministic(sq):
     print("linear determinism", flush=True)
     p, wc, ws = _random_problem(256, 512, 2048, seed=1)
-    a = to_np(sq.linear(oracle_prepared(p), sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws))))
-    b = to_np(sq.linear(oracle_prepared(p), sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(ws))))
+    a = to_np(sq.linear(oracle_prepared(p), w_to_gpu(wc, ws)))
+    b = to_np(sq.linear(oracle_prepared(p), w_to_gpu(wc, ws)))
     assert np.array_equal(a, b)
 
 
@@ -94,7 +98,7 @@ def test_linear_128x4096_full(sq):
     prep = sq.prepare(bf16_to_gpu(wl["x"]), None, 2, 4)
     wq = sq.quantize_mxfp4(bf16_to_gpu(wl["w"]))
     assert_prepare_equal(prep, p)
-    assert np.array_equal(to_np(wq.codes), wc) and np.array_equal(to_np(wq.scales), ws)
+    assert np.array_equal(to_np(wq.codes), wc) and np.array_equal(w_scales_rows(wq.scales, ws.shape[1]), ws)
     y = sq.linear(prep, wq)
     y_ref, bound = linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
     assert_y_close(to_np(y), y_ref, bound)
@@ -108,7 +112,8 @@ def _sampled_linear_check(sq, x, gamma, n, m, w_bits, rows, cols):
     p = prepare_ref(x[rows], gamma, n, m)
     assert_prepare_equal(prep, p, rows=rows)
     wc, ws = quantize_weight_ref(w_bits[cols])
-    assert np.array_equal(to_np(wq.codes)[cols], wc) and np.array_equal(to_np(wq.scales)[cols], ws)
+    assert np.array_equal(to_np(wq.codes)[cols], wc)
+    assert np.array_equal(w_scales_rows(wq.scales, ws.shape[1])[cols], ws)
     y_ref, bound = linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
     assert_y_close(to_np(y)[np.ix_(rows, cols)], y_ref, bound)
 

@@ -12,7 +12,7 @@ import pytest
 from oracle import prepare_ref, quantize_weight_ref
 from synth import (adversarial_rows, bf16_round, bf16_to_f32, workload_down_silu, workload_linear,
                    workload_llama70b_decode, workload_llama8b_mlp, workload_qwen3_moe)
-from gpu_util import assert_prepare_equal, bf16_to_gpu, to_np
+from gpu_util import assert_prepare_equal, bf16_to_gpu, to_np, w_scales_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,7 @@ def test_prepare_strided_rows_single_block_and_no_mask(sq):
     assert_prepare_equal(sq.prepare(bf16_to_gpu(one), None, 8, 16), prepare_ref(one, None, 8, 16))
     # T = 0 is a no-op that returns empty outputs
     empty = sq.prepare(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), None, 2, 4)
-    assert empty.bb_codes.shape == (0, 32)
+    assert empty.bb_codes.shape == (0, 32) and empty.bb_scales.shape == (1, 0, 4)
 
 
 def test_prepare_deterministic(sq):
@@ -130,7 +130,7 @@ def test_quantize_exhaustive_bf16(sq):
     assert np.array_equal(bf16_to_f32(rows), x)
     wc, ws = quantize_weight_ref(rows)
     got = sq.quantize_mxfp4(bf16_to_gpu(rows))
-    assert np.array_equal(to_np(got.scales), ws)
+    assert np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
     assert np.array_equal(to_np(got.codes), wc)
 
 
@@ -139,11 +139,11 @@ def test_quantize_weights_and_ragged(sq):
     w = workload_linear(T=8, K=4096, O=4096)["w"]
     wc, ws = quantize_weight_ref(w)
     got = sq.quantize_mxfp4(bf16_to_gpu(w))
-    assert np.array_equal(to_np(got.codes), wc) and np.array_equal(to_np(got.scales), ws)
+    assert np.array_equal(to_np(got.codes), wc) and np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
     xb = _mixed_input(33, 160, 3)
     wc, ws = quantize_weight_ref(xb)
     got = sq.quantize_mxfp4(bf16_to_gpu(xb))
-    assert np.array_equal(to_np(got.codes), wc) and np.array_equal(to_np(got.scales), ws)
+    assert np.array_equal(to_np(got.codes), wc) and np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
 
 
 def _rows_sample(T, count, seed):

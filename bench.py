@@ -197,6 +197,44 @@ def build_workload(name, torch, sq):
     raise SystemExit(f"unknown workload {name}; choose from {WORKLOADS}")
 
 
+KERNEL_SOURCES = {"gemm": "gemm.hip", "prepare": "prepare.hip", "silu": "glue.hip", "grouped": "gemm.hip"}
+
+
+def source_digest(stage_name):
+    """sha256 of the HIP source that implements a stage (ties recorded counters to a kernel version)."""
+    import hashlib
+    key = "gemm" if "gemm" in stage_name or "grouped" in stage_name else (
+        "silu" if "silu" in stage_name else "prepare")
+    path = os.path.join(ROOT, "activation_sparsity_fp4_amd", "csrc", KERNEL_SOURCES[key])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload, stage_name):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE (profiles/traffic.json),
+    or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(f"{workload}/{stage_name}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_digest(stage_name):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(n_bytes, steps):
+    """Device-to-device copy of n_bytes, repeated: the reference for counter scaling."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n_bytes, "steps": steps}), flush=True)
+
+
 def cpu_baseline(oracle_sample, tokens_full, budget_s=20.0):
     """Time the CPU oracle on a bounded row sample; grow the sample until it takes
     a few seconds, stop before the budget."""
@@ -226,6 +264,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_mlp", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-stage", default=None,
+                    help="run only this stage in warmup and timing (per-kernel profiling; not a step)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a device copy of this many bytes (reference for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -237,9 +279,16 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs the GPU")
     torch.cuda.init()
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, args.steps)
+        return
     print(f"# building inputs for {args.workload}", file=sys.stderr, flush=True)
     stages, tokens, cfg, oracle_sample = build_workload(args.workload, torch, sq)
     torch.cuda.synchronize()
+    if args.profile_stage:
+        stages = [s for s in stages if s.name == args.profile_stage]
+        if not stages:
+            raise SystemExit(f"no stage {args.profile_stage!r} in workload {args.workload}")
 
     for _ in range(args.warmup):
         for s in stages:
@@ -278,14 +327,18 @@ def main():
     # dominant kernel: the stage with the largest average duration
     dom_i = int(np.argmax(stage_ms))
     dom = stages[dom_i]
+    traffic = recorded_traffic(args.workload, dom.name)
     if dom.kind == "mfma":
         ach = dom.flops_alg / (stage_ms[dom_i] * 1e-3) / 1e12
         roof = {"kernel": dom.name, "bound": "mfma", "achieved": round(ach, 1), "peak": FP4_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / FP4_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / FP4_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         ach = dom.bytes / (stage_ms[dom_i] * 1e-3) / 1e9
         roof = {"kernel": dom.name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+    if traffic is not None:
+        roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roof["algorithmic_bytes"] = round(dom.bytes)
 
     value = tokens * args.steps / wall
     line = {
@@ -294,7 +347,10 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4", "data": "synthetic", "config": cfg, "roofline": roof, "stages": breakdown,
     }
-    if oracle_sample is not None and not args.no_cpu_baseline:
+    if args.profile_stage:
+        line["profile_stage"] = args.profile_stage
+        line["note"] = "only this stage was run; value and ms_per_step are not a full step"
+    if oracle_sample is not None and not args.no_cpu_baseline and not args.profile_stage:
         print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(oracle_sample, tokens)
     else:

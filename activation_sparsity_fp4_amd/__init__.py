@@ -30,22 +30,26 @@ __all__ = [
 
 
 class Prepared(NamedTuple):
-    """Outputs of the prepare operator (all uint8 device tensors).
+    """Outputs of the prepare operator (uint8 device tensors) and K.
 
-    Scales are stage-major: [ceil(K/128), T, 4], byte (k // 32) % 4 of entry
-    [k // 128, t]; bytes past the last block of a row are zero."""
-    bb_codes: "object"    # [T, K/2]
-    bb_scales: "object"   # [G, T, 4], G = ceil(K/128)
-    res_codes: "object"   # [T, K/2]
+    Codes and scales are stage-major with G = ceil(K/128) stages of 128 K
+    entries: the 16 code bytes of block b = k // 32 of row t sit at
+    codes[b // 4, t, 16 * (b % 4):][:16] and its scale byte at
+    scales[b // 4, t, b % 4]; blocks past K // 32 are zero."""
+    bb_codes: "object"    # [G, T, 64]
+    bb_scales: "object"   # [G, T, 4]
+    res_codes: "object"   # [G, T, 64]
     res_scales: "object"  # [G, T, 4]
-    mask: "object"        # [T, K/8] or None
+    mask: "object"        # [T, K/8] (row-major bitmap) or None
+    K: int
 
 
 class MXFP4(NamedTuple):
-    """A block-scaled FP4 tensor: codes [R, K/2] with stage-major scales
-    [G, R, 4]; for expert weights codes [E, O, K/2] and scales [E, G, O, 4]."""
+    """A block-scaled FP4 tensor, stage-major: codes [G, R, 64] and scales
+    [G, R, 4]; for expert weights codes [E, G, O, 64] and scales [E, G, O, 4]."""
     codes: "object"
     scales: "object"
+    K: int
 
 
 def stages(K: int) -> int:
@@ -79,6 +83,24 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims")
 
 
+def _check_stage_major(codes, scales, R, K, name):
+    G = stages(K)
+    if tuple(codes.shape) != (G, R, 64) or tuple(scales.shape) != (G, R, 4):
+        raise ValueError(f"{name}: expected stage-major codes [{G}, {R}, 64] and scales [{G}, {R}, 4], "
+                         f"got {tuple(codes.shape)} and {tuple(scales.shape)}")
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError(f"{name}: codes and scales must be contiguous")
+
+
+def _check_prepared(prep):
+    torch = _torch()
+    for name in ("bb_codes", "res_codes", "bb_scales", "res_scales"):
+        _need(getattr(prep, name), torch.uint8, name, 3)
+    T = prep.bb_codes.shape[1]
+    _check_stage_major(prep.bb_codes, prep.bb_scales, T, prep.K, "backbone")
+    _check_stage_major(prep.res_codes, prep.res_scales, T, prep.K, "residual")
+
+
 def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: Optional[Prepared] = None) -> Prepared:
     """Fused prepare: N:M mask, MXFP4 backbone, residual against it, MXFP4 residual."""
     torch = _torch()
@@ -92,9 +114,11 @@ def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: 
     if out is None:
         kw = dict(dtype=torch.uint8, device=x.device)
         G = stages(K)
-        out = Prepared(torch.empty((T, K // 2), **kw), torch.empty((G, T, 4), **kw),
-                       torch.empty((T, K // 2), **kw), torch.empty((G, T, 4), **kw),
-                       torch.empty((T, K // 8), **kw) if with_mask else None)
+        out = Prepared(torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
+                       torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
+                       torch.empty((T, K // 8), **kw) if with_mask else None, K)
+    elif out.K != K:
+        raise ValueError("out was allocated for another K")
     st = _lib.call("sharq_prepare", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), n, m,
                    out.bb_codes.data_ptr(), out.bb_scales.data_ptr(), out.res_codes.data_ptr(),
                    out.res_scales.data_ptr(), _ptr(out.mask), _stream(x.device))
@@ -110,18 +134,18 @@ def quantize_mxfp4(x, out: Optional[MXFP4] = None) -> MXFP4:
     if x.dim() == 3:
         E, R, K = x.shape
         if out is None:
-            out = MXFP4(torch.empty((E, R, K // 2), dtype=torch.uint8, device=x.device),
-                        torch.empty((E, stages(K), R, 4), dtype=torch.uint8, device=x.device))
+            out = MXFP4(torch.empty((E, stages(K), R, 64), dtype=torch.uint8, device=x.device),
+                        torch.empty((E, stages(K), R, 4), dtype=torch.uint8, device=x.device), K)
         for e in range(E):
-            quantize_mxfp4(x[e], MXFP4(out.codes[e], out.scales[e]))
+            quantize_mxfp4(x[e], MXFP4(out.codes[e], out.scales[e], K))
         return out
     _need(x, torch.bfloat16, "x", 2)
     if x.stride(1) != 1:
         raise ValueError("x rows must be contiguous along K")
     R, K = x.shape
     if out is None:
-        out = MXFP4(torch.empty((R, K // 2), dtype=torch.uint8, device=x.device),
-                    torch.empty((stages(K), R, 4), dtype=torch.uint8, device=x.device))
+        out = MXFP4(torch.empty((stages(K), R, 64), dtype=torch.uint8, device=x.device),
+                    torch.empty((stages(K), R, 4), dtype=torch.uint8, device=x.device), K)
     st = _lib.call("sharq_quantize_mxfp4", x.data_ptr(), R, K, x.stride(0), out.codes.data_ptr(),
                    out.scales.data_ptr(), _stream(x.device))
     _lib.check("sharq_quantize_mxfp4", st)
@@ -131,17 +155,14 @@ def quantize_mxfp4(x, out: Optional[MXFP4] = None) -> MXFP4:
 def linear(prep: Prepared, w: MXFP4, out=None):
     """Two-path FP4 GEMM: Y = deq(backbone) W^T + deq(residual) W^T, fp32 [T, O]."""
     torch = _torch()
-    for name in ("bb_codes", "res_codes"):
-        _need(getattr(prep, name), torch.uint8, name, 2)
-    for name in ("bb_scales", "res_scales"):
-        _need(getattr(prep, name), torch.uint8, name, 3)
-    _need(w.codes, torch.uint8, "w.codes", 2)
+    _check_prepared(prep)
+    _need(w.codes, torch.uint8, "w.codes", 3)
     _need(w.scales, torch.uint8, "w.scales", 3)
-    T, Kh = prep.bb_codes.shape
-    O = w.codes.shape[0]
-    K = 2 * Kh
-    if w.codes.shape[1] != Kh:
+    T, K = prep.bb_codes.shape[1], prep.K
+    O = w.codes.shape[1]
+    if w.K != K:
         raise ValueError("weight K does not match the activation K")
+    _check_stage_major(w.codes, w.scales, O, K, "w")
     if out is None:
         out = torch.empty((T, O), dtype=torch.float32, device=prep.bb_codes.device)
     _need(out, torch.float32, "out", 2)
@@ -153,25 +174,29 @@ def linear(prep: Prepared, w: MXFP4, out=None):
 
 
 def linear_grouped(prep: Prepared, w: MXFP4, seg_offsets, a_rows=None, out=None):
-    """Grouped two-path GEMM over expert segments. w.codes is [E, O, K/2];
+    """Grouped two-path GEMM over expert segments. w.codes is [E, G, O, 64];
     seg_offsets int32 [E+1]; a_rows int32 [P] (source row of each sorted pair) or None."""
     torch = _torch()
-    _need(w.codes, torch.uint8, "w.codes", 3)
+    _check_prepared(prep)
+    _need(w.codes, torch.uint8, "w.codes", 4)
     _need(w.scales, torch.uint8, "w.scales", 4)
     _need(seg_offsets, torch.int32, "seg_offsets", 1)
-    E, O, Kh = w.codes.shape
-    K = 2 * Kh
+    E, _, O, _ = w.codes.shape
+    K = prep.K
+    if w.K != K:
+        raise ValueError("weight K does not match the activation K")
+    _check_stage_major(w.codes[0], w.scales[0], O, K, "w")
     if seg_offsets.numel() != E + 1:
         raise ValueError("seg_offsets must have E + 1 entries")
     if a_rows is not None:
         _need(a_rows, torch.int32, "a_rows", 1)
         P = a_rows.numel()
     else:
-        P = prep.bb_codes.shape[0]
+        P = prep.bb_codes.shape[1]
     if out is None:
         out = torch.empty((P, O), dtype=torch.float32, device=w.codes.device)
     st = _lib.call("sharq_linear_grouped", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
-                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), prep.bb_codes.shape[0], _ptr(a_rows),
+                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), prep.bb_codes.shape[1], _ptr(a_rows),
                    seg_offsets.data_ptr(), E, w.codes.data_ptr(), w.scales.data_ptr(), P, O, K, out.data_ptr(),
                    _stream(out.device))
     _lib.check("sharq_linear_grouped", st)

@@ -15,7 +15,8 @@
 // Tiling: a 256-thread workgroup computes a 128 (rows) x 256 (outputs) tile;
 // wave w covers rows 64*(w&1) .. +64 and outputs 128*(w>>1) .. +128, i.e. 2 x 4
 // MFMA tiles of 32 x 32. K advances 128 entries per stage (64 bytes of codes
-// per row per operand). A stage holds the backbone tile, the residual tile, the
+// per row per operand; with the stage-major layout of sharq_device.h one stage
+// of a tile is one contiguous run of every operand). A stage holds the backbone tile, the residual tile, the
 // weight tile and their scales (34 KB of LDS).
 //
 // Main path (K % 128 == 0): a ring of 4 LDS stages filled by buffer loads that
@@ -29,9 +30,9 @@
 // c ^ ((r >> 2) & 3), which keeps the rows read by one MFMA fragment on
 // distinct banks of the 64-bank LDS.
 //
-// Scales are stored stage-major ([K/128][rows][4], see sharq_device.h): one
-// stage of a 128-row tile is a single contiguous 512-byte run, so the scale
-// loads cost a few L2 requests per stage rather than one per row.
+// Codes and scales are stored stage-major (sharq_device.h): one stage of a
+// 128-row tile is a contiguous 8 KB run of codes and a 512-byte run of
+// scales, so every load uses whole cache lines.
 //
 // MFMA operand layouts (32x32x64, FP4): lane l holds row (l % 32) and the 32
 // consecutive K entries of block (l / 32) of the 64-entry K slice, low nibble
@@ -118,10 +119,10 @@ __device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[2][
 }
 
 struct Operands {
-  const uint8_t* a_codes[2];   // backbone, residual codes [rows][K/2]
-  const uint8_t* a_scales[2];  // [rows][K/32]
-  const uint8_t* w_codes;      // [O][K/2]  (already offset to the expert)
-  const uint8_t* w_scales;     // [O][K/32]
+  const uint8_t* a_codes[2];   // backbone, residual codes [G][rows][64] (stage-major)
+  const uint8_t* a_scales[2];  // [G][rows][4]
+  const uint8_t* w_codes;      // [G][O][64]  (already offset to the expert)
+  const uint8_t* w_scales;     // [G][O][4]
   int64_t a_rows_total;        // rows addressable through a_codes (bounds of the buffer view)
   int64_t K;
   int64_t O;
@@ -176,12 +177,12 @@ __device__ __forceinline__ void buffer_to_lds4(i32x4 rsrc, uint32_t voff, uint32
 
 struct RingLoader {
   i32x4 a_codes[2], a_scales[2], w_codes, w_scales;
-  uint32_t a_off[2];   // byte offset of this lane's A code chunk rows (chunks j = 0, 1), kOOB if absent
+  uint32_t a_off[2];   // byte offset of this lane's A code chunk inside a stage (chunks j = 0, 1), kOOB if absent
   uint32_t w_off[4];   // same for the 4 W chunks
   uint32_t s_off[2];   // scale-row byte offsets for this wave's two scale instructions
   int wave;            // wave-uniform
   int nsteps;
-  uint32_t a_stage_bytes, w_stage_bytes;  // scale bytes of one stage: 4 per row
+  uint32_t a_stage_bytes, w_stage_bytes;  // scale bytes of one stage: 4 per row (codes: 64 per row)
 
   // Issue the 10 loads of stage s (K entries [128 s, 128 s + 128)) into `st`.
   // Past the last stage every offset is moved out of range: the loads keep
@@ -189,17 +190,18 @@ struct RingLoader {
   __device__ __forceinline__ void issue(uint8_t* st, int s) const {
     const uint32_t base = lds_offset(st);
     const bool live = s < nsteps;
-    const uint32_t kc = live ? (uint32_t)s * kRowBytes : kOOB;
+    const uint32_t ka = live ? (uint32_t)s * a_stage_bytes * 16 : kOOB;  // stage start in the code arrays
+    const uint32_t kw = live ? (uint32_t)s * w_stage_bytes * 16 : kOOB;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int chunk = wave + 4 * j;  // 1 KB chunk inside the 8 KB A tile
-      buffer_to_lds16(a_codes[0], a_off[j] + kc, base + kOffAs + 1024 * chunk);
-      buffer_to_lds16(a_codes[1], a_off[j] + kc, base + kOffAr + 1024 * chunk);
+      buffer_to_lds16(a_codes[0], a_off[j] + ka, base + kOffAs + 1024 * chunk);
+      buffer_to_lds16(a_codes[1], a_off[j] + ka, base + kOffAr + 1024 * chunk);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int chunk = wave + 4 * j;  // 1 KB chunk inside the 16 KB W tile
-      buffer_to_lds16(w_codes, w_off[j] + kc, base + kOffW + 1024 * chunk);
+      buffer_to_lds16(w_codes, w_off[j] + kw, base + kOffW + 1024 * chunk);
     }
     const uint32_t ksa = live ? (uint32_t)s * a_stage_bytes : kOOB;
     const uint32_t ksw = live ? (uint32_t)s * w_stage_bytes : kOOB;
@@ -319,16 +321,16 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 31, lh = lane >> 5;
-  const int64_t kbytes = op.K >> 1, kblocks = op.K >> 5;
+  const int64_t G = op.nsteps;
 
   RingLoader ld;
   ld.wave = wave;
-  ld.a_codes[0] = make_rsrc(op.a_codes[0], op.a_rows_total * kbytes);
-  ld.a_codes[1] = make_rsrc(op.a_codes[1], op.a_rows_total * kbytes);
-  ld.a_scales[0] = make_rsrc(op.a_scales[0], op.a_rows_total * kblocks);
-  ld.a_scales[1] = make_rsrc(op.a_scales[1], op.a_rows_total * kblocks);
-  ld.w_codes = make_rsrc(op.w_codes, op.O * kbytes);
-  ld.w_scales = make_rsrc(op.w_scales, op.O * kblocks);
+  ld.a_codes[0] = make_rsrc(op.a_codes[0], op.a_rows_total * G * kRowBytes);
+  ld.a_codes[1] = make_rsrc(op.a_codes[1], op.a_rows_total * G * kRowBytes);
+  ld.a_scales[0] = make_rsrc(op.a_scales[0], op.a_rows_total * G * 4);
+  ld.a_scales[1] = make_rsrc(op.a_scales[1], op.a_rows_total * G * 4);
+  ld.w_codes = make_rsrc(op.w_codes, op.O * G * kRowBytes);
+  ld.w_scales = make_rsrc(op.w_scales, op.O * G * 4);
   ld.a_stage_bytes = (uint32_t)(op.a_rows_total * 4);
   ld.w_stage_bytes = (uint32_t)(op.O * 4);
   // The LDS chunk position a lane fills is fixed (lane * 16 inside its 1 KB
@@ -338,14 +340,14 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
     const int row = 16 * (wave + 4 * j) + (lane >> 2);
     const int part = (lane & 3) ^ swz_part(row);
     const int64_t src = tr.src(row);
-    ld.a_off[j] = src >= 0 ? (uint32_t)(src * kbytes + part * 16) : kOOB;
+    ld.a_off[j] = src >= 0 ? (uint32_t)(src * kRowBytes + part * 16) : kOOB;
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 16 * (wave + 4 * j) + (lane >> 2);
     const int part = (lane & 3) ^ swz_part(row);
     const int64_t o = n0 + row;
-    ld.w_off[j] = o < op.O ? (uint32_t)(o * kbytes + part * 16) : kOOB;
+    ld.w_off[j] = o < op.O ? (uint32_t)(o * kRowBytes + part * 16) : kOOB;
   }
   {
     const int64_t src = tr.src(64 * (wave & 1) + lane);
@@ -399,18 +401,19 @@ __device__ __forceinline__ uint32_t load_scales4(const uint8_t* scales, int64_t 
 __device__ __forceinline__ void load_stage_regs(Prefetch& pf, const Operands& op, int s, int tid,
                                                 const int64_t (&a_src)[2], int64_t a_src_scale,
                                                 const int64_t (&w_row)[4], int64_t w_row_scale) {
-  const int r0 = tid >> 2, part = tid & 3;
-  const int64_t kbytes = op.K >> 1;
-  const int64_t col = (int64_t)s * kRowBytes + part * 16;
-  const bool col_ok = col < kbytes;
-  (void)r0;
+  const int part = tid & 3;
+  // block `part` of the stage exists (the padding blocks of a last, partial
+  // stage are zero in a well-formed tensor; they are not read)
+  const bool col_ok = 4 * (int64_t)s + part < (op.K >> 5);
+  const int64_t a_stage = (int64_t)s * op.a_rows_total * kRowBytes + part * 16;
+  const int64_t w_stage = (int64_t)s * op.O * kRowBytes + part * 16;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int64_t r = a_src[c];
     const bool ok = r >= 0 && col_ok;
-    const int64_t rr = ok ? r : 0;
-    const uint4 v0 = *reinterpret_cast<const uint4*>(op.a_codes[0] + rr * kbytes + (ok ? col : 0));
-    const uint4 v1 = *reinterpret_cast<const uint4*>(op.a_codes[1] + rr * kbytes + (ok ? col : 0));
+    const int64_t off = ok ? a_stage + r * kRowBytes : 0;
+    const uint4 v0 = *reinterpret_cast<const uint4*>(op.a_codes[0] + off);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(op.a_codes[1] + off);
     pf.a[0][c] = ok ? v0 : make_uint4(0, 0, 0, 0);
     pf.a[1][c] = ok ? v1 : make_uint4(0, 0, 0, 0);
   }
@@ -418,7 +421,7 @@ __device__ __forceinline__ void load_stage_regs(Prefetch& pf, const Operands& op
   for (int c = 0; c < 4; ++c) {
     const int64_t r = w_row[c];
     const bool ok = r >= 0 && col_ok;
-    const uint4 v = *reinterpret_cast<const uint4*>(op.w_codes + (ok ? r : 0) * kbytes + (ok ? col : 0));
+    const uint4 v = *reinterpret_cast<const uint4*>(op.w_codes + (ok ? w_stage + r * kRowBytes : 0));
     pf.w[c] = ok ? v : make_uint4(0, 0, 0, 0);
   }
   const int64_t kblocks = op.K >> 5;
@@ -587,8 +590,8 @@ __global__ __launch_bounds__(kThreads) void linear_grouped_kernel(
   tr.rows_valid = hi - tr.m0 < kBM ? hi - tr.m0 : kBM;
   tr.gather = a_rows;
   const int64_t n0 = (int64_t)blockIdx.x * kBN;
-  op.w_codes = w_codes_all + (int64_t)e * op.O * (op.K >> 1);
-  op.w_scales = w_scales_all + (int64_t)e * op.O * 4 * op.nsteps;  // [E][K/128 stages][O][4]
+  op.w_codes = w_codes_all + (int64_t)e * op.O * kRowBytes * op.nsteps;  // [E][G][O][64]
+  op.w_scales = w_scales_all + (int64_t)e * op.O * 4 * op.nsteps;          // [E][G][O][4]
   v16f acc[2][4];
   zero_acc(acc);
   if constexpr (kRingPath)

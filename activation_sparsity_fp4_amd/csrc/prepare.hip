@@ -104,11 +104,9 @@ __device__ __forceinline__ uint32_t select_exact(const float (&x)[32]) {
 
 // Lane -> (row, block) map shared by the prepare and quantise kernels. A wave
 // owns a band of 16 rows and one 128-entry K stage (4 blocks): lane l takes
-// row 16 * band + l / 4 and block 4 * stage + l % 4. Its 64 stage-major scale
-// bytes are then one contiguous run, each row's input is read in 256-byte
-// runs and its codes written in 64-byte runs; consecutive waves walk the
-// stages of a band, so the two halves of a code cache line are written by
-// neighbouring waves.
+// row 16 * band + l / 4 and block 4 * stage + l % 4. In the stage-major
+// layout its codes are then one contiguous 1 KB run per code array and its
+// scales one 64-byte run; each row's input is read in 256-byte runs.
 struct BlockOfLane {
   uint32_t t, b;
   bool row_ok, block_ok;
@@ -136,8 +134,10 @@ __global__ __launch_bounds__(256) void prepare_kernel(
     uint8_t* __restrict__ mask_out) {
   const BlockOfLane lb = block_of_lane(stages, blocks_per_row, rows);
   if (!lb.block_ok) {
-    // the unused bytes of a last, partial stage are zero
+    // the unused blocks of a last, partial stage are zero
     if (lb.row_ok) {
+      *reinterpret_cast<uint4*>(bb_codes + code_offset(lb.t, lb.b, rows)) = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(res_codes + code_offset(lb.t, lb.b, rows)) = make_uint4(0, 0, 0, 0);
       bb_scales[scale_index(lb.t, lb.b, rows)] = 0;
       res_scales[scale_index(lb.t, lb.b, rows)] = 0;
     }
@@ -207,9 +207,8 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   const uint32_t e_rs = e8m0_from_amax_bits(amax_bits32(r));
   const uint4 c_rs = quantize32(r, scale_from_e8m0(e_rs));
 
-  const int64_t row_codes = (int64_t)blocks_per_row * (kBlock / 2);
-  reinterpret_cast<uint4*>(bb_codes + (int64_t)t * row_codes)[b] = c_bb;
-  reinterpret_cast<uint4*>(res_codes + (int64_t)t * row_codes)[b] = c_rs;
+  *reinterpret_cast<uint4*>(bb_codes + code_offset(t, b, rows)) = c_bb;
+  *reinterpret_cast<uint4*>(res_codes + code_offset(t, b, rows)) = c_rs;
   bb_scales[scale_index(t, b, rows)] = (uint8_t)e_bb;
   res_scales[scale_index(t, b, rows)] = (uint8_t)e_rs;
   if (mask_out) reinterpret_cast<uint32_t*>(mask_out)[gid] = keep;
@@ -222,7 +221,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const BlockOfLane lb = block_of_lane(stages, blocks_per_row, rows);
   if (!lb.block_ok) {
-    if (lb.row_ok) scales[scale_index(lb.t, lb.b, rows)] = 0;
+    if (lb.row_ok) {
+      *reinterpret_cast<uint4*>(codes + code_offset(lb.t, lb.b, rows)) = make_uint4(0, 0, 0, 0);
+      scales[scale_index(lb.t, lb.b, rows)] = 0;
+    }
     return;
   }
   const uint32_t t = lb.t, b = lb.b;
@@ -240,8 +242,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(
   }
   const uint32_t e = e8m0_from_amax_bits(amax_bits32(xv));
   const uint4 c = quantize32(xv, scale_from_e8m0(e));
-  const int64_t row_codes = (int64_t)blocks_per_row * (kBlock / 2);
-  reinterpret_cast<uint4*>(codes + (int64_t)t * row_codes)[b] = c;
+  *reinterpret_cast<uint4*>(codes + code_offset(t, b, rows)) = c;
   scales[scale_index(t, b, rows)] = (uint8_t)e;
 }
 

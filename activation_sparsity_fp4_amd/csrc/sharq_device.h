@@ -65,13 +65,20 @@ __device__ __forceinline__ void dequantize32(uint4 c, float scale, float (&q)[32
   }
 }
 
-// Scale layout shared by every kernel: the E8M0 bytes of a [rows x K] MXFP4
-// tensor are grouped by 128-entry K stage, [ceil(K/128)][rows][4]: byte
-// (k / 32) % 4 of the dword for (stage k / 128, row). One GEMM stage of a row
-// tile then reads one contiguous run of dwords instead of one scattered byte
-// run per row. Bytes of a last, partial stage past K / 32 blocks are zero.
+// Layout shared by every kernel: an MXFP4 [rows x K] tensor is stored
+// stage-major, grouped by 128-entry K stage (G = ceil(K/128) stages).
+//   codes  [G][rows][64]: the 16 code bytes of block b of a row sit at byte
+//          16 * (b % 4) of the row's 64-byte chunk in stage b / 4;
+//   scales [G][rows][4]:  the E8M0 byte of block b is byte b % 4 of the row's
+//          dword in stage b / 4.
+// One GEMM stage of a row tile is then one contiguous run of codes and one of
+// scales, so its loads use whole cache lines. Blocks of a last, partial stage
+// past K / 32 have zero codes and zero scale bytes.
 __device__ __forceinline__ int64_t scale_index(int64_t row, uint32_t block, int64_t rows) {
   return (int64_t)(block >> 2) * rows * 4 + row * 4 + (block & 3);
+}
+__device__ __forceinline__ int64_t code_offset(int64_t row, uint32_t block, int64_t rows) {
+  return (int64_t)(block >> 2) * rows * 64 + row * 64 + (block & 3) * 16;
 }
 
 // Largest |v| of 32 floats as a bit pattern (sign cleared). Integer max on

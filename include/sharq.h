@@ -16,11 +16,17 @@
  * floor(log2(block amax)) - 2, clamped to [-127, 127], -127 for an all-zero
  * block; codes round to nearest with ties to the even code and saturate at 6.
  *
- * Scale layout ("stage-major"): for a tensor of R rows and K entries per row,
- * scales are u8 [G][R][4] with G = ceil(K / 128): the byte of block b
- * (K entries [32 b, 32 b + 32)) of row r sits at [b / 4][r][b % 4]. Bytes of
- * a last, partial stage past K / 32 blocks are zero. One GEMM stage of 128 K
- * entries of a row tile is then one contiguous run of scale dwords.
+ * Layout ("stage-major"): a tensor of R rows and K entries per row is cut
+ * into G = ceil(K / 128) stages of 128 K entries (4 blocks of 32), stored one
+ * stage after the other:
+ *   codes  u8 [G][R][64]: the 16 code bytes of block b (K entries
+ *          [32 b, 32 b + 32)) of row r sit at [b / 4][r][16 (b % 4) .. +16),
+ *          two codes per byte, the even K index in the low nibble;
+ *   scales u8 [G][R][4]:  the scale byte of block b of row r sits at
+ *          [b / 4][r][b % 4].
+ * Blocks of a last, partial stage past K / 32 have zero codes and zero scale
+ * bytes (the quantisers write them; inputs from elsewhere must hold zeros).
+ * One GEMM stage of a row tile is then one contiguous run of each operand.
  *
  * Conventions for every entry point below:
  *  - Pointers are DEVICE pointers unless stated otherwise; the caller owns
@@ -33,8 +39,8 @@
  *  - A call with no rows (T, P or O equal to 0) is a no-op that returns
  *    SHARQ_OK once the shape arguments are valid; its pointers may be NULL.
  *  - Inputs must be finite; with NaN or Inf the outputs are unspecified.
- *  - Row-major layouts; sizes are element counts. T = rows (tokens),
- *    K = input features, O = output features.
+ *  - Activations and outputs are row-major; sizes are element counts.
+ *    T = rows (tokens), K = input features, O = output features.
  *  - Alignment: every pointer 16-byte aligned; ldx a multiple of 8.
  */
 #ifndef SHARQ_H
@@ -63,7 +69,7 @@ typedef enum {
 /* Host. Static string describing a status code; never NULL. */
 SHARQ_API const char* sharq_status_string(int status);
 
-/* Host. Version of this ABI (bumped on any signature change). */
+/* Host. Version of this ABI (bumped on any signature or layout change). */
 SHARQ_API int sharq_abi_version(void);
 
 /*
@@ -76,9 +82,9 @@ SHARQ_API int sharq_abi_version(void);
  *  n, m     N:M pattern: (2,4) or (8,16). Selection keeps, in each group of m
  *           consecutive K entries, the n largest |x'|; equal |x'| go to the
  *           lower index.
- *  bb_codes   u8 [T][K/2]   backbone E2M1 codes (0x0 at dropped positions)
+ *  bb_codes   u8 [G][T][64] backbone E2M1 codes (0x0 at dropped positions)
  *  bb_scales  u8 [G][T][4]  backbone E8M0 scales, stage-major
- *  res_codes  u8 [T][K/2]   residual codes, residual r = x' - dequant(backbone)
+ *  res_codes  u8 [G][T][64] residual codes, residual r = x' - dequant(backbone)
  *  res_scales u8 [G][T][4]  residual scales, stage-major
  *  mask       u8 [T][K/8]   bit (k & 7) of byte k >> 3 set when k is kept, or
  *                           NULL to skip writing it.
@@ -95,7 +101,7 @@ SHARQ_API int sharq_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx
  * sharq_quantize_mxfp4 -- plain MXFP4 of bf16 rows along K (no mask, no
  * residual), the same element and scale rules as sharq_prepare. Used to
  * produce the pre-quantised weight [O][K] that sharq_linear reads.
- *  x bf16 [T][ldx]; codes u8 [T][K/2]; scales u8 [G][T][4] (stage-major).
+ *  x bf16 [T][ldx]; codes u8 [G][T][64]; scales u8 [G][T][4] (stage-major).
  * Requires K % 32 == 0, ldx >= K, T * K / 32 < 2^31.
  */
 SHARQ_API int sharq_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx,
@@ -107,8 +113,8 @@ SHARQ_API int sharq_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t K, int6
  * weight load; Section 1: the residual path accumulates into the sparse
  * output):
  *   Y[t][o] = sum_k deq(bb)[t][k] * deq(W)[o][k] + sum_k deq(res)[t][k] * deq(W)[o][k]
- *  bb_codes/res_codes u8 [T][K/2], bb_scales/res_scales u8 [G][T][4] (as
- *  written by sharq_prepare); w_codes u8 [O][K/2], w_scales u8 [G][O][4]
+ *  bb_codes/res_codes u8 [G][T][64], bb_scales/res_scales u8 [G][T][4] (as
+ *  written by sharq_prepare); w_codes u8 [G][O][64], w_scales u8 [G][O][4]
  *  (as written by sharq_quantize_mxfp4); y fp32 [T][ldy], overwritten (not
  *  accumulated into).
  * Accumulation is fp32 in an unspecified order. Requires K % 32 == 0,
@@ -126,12 +132,12 @@ SHARQ_API int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales,
  * Output row p (0 <= p < P) belongs to the expert e with
  * seg_offsets[e] <= p < seg_offsets[e+1]; it reads activation row a_rows[p]
  * (or row p when a_rows is NULL) and expert e's weight.
- *  bb_codes/res_codes u8 [T_src][K/2], bb_scales/res_scales u8 [G][T_src][4]
+ *  bb_codes/res_codes u8 [G][T_src][64], bb_scales/res_scales u8 [G][T_src][4]
  *              the prepared activation rows (T_src >= P when a_rows is NULL).
  *  a_rows      i32 [P] device, each in [0, T_src), or NULL.
  *  seg_offsets i32 [E+1] device, non-decreasing, [0] = 0, [E] = P.
- *  w_codes u8 [E][O][K/2], w_scales u8 [E][G][O][4] (each expert's scales
- *              stage-major); y fp32 [P][O].
+ *  w_codes u8 [E][G][O][64], w_scales u8 [E][G][O][4] (each expert's
+ *              tensor stage-major); y fp32 [P][O].
  * Segment and gather contents are read on the device; their validity is a
  * precondition (a gathered row outside [0, T_src) reads as zeros).
  */

@@ -60,13 +60,37 @@ def row_major(s_stage, kblocks):
     return flat[:, :kblocks]
 
 
+def codes_stage_major(c_rows):
+    """Row-major codes [R, K/2] (the oracle's form) -> the library's stage-major
+    [ceil(K/128), R, 64] layout, zero past the last block. Pure data movement."""
+    c_rows = np.asarray(c_rows, dtype=np.uint8)
+    R, kh = c_rows.shape
+    G = (kh + 63) // 64
+    pad = np.zeros((R, 64 * G), dtype=np.uint8)
+    pad[:, :kh] = c_rows
+    return np.ascontiguousarray(pad.reshape(R, G, 64).transpose(1, 0, 2))
+
+
+def codes_row_major(c_stage, kbytes):
+    """Stage-major codes [G, R, 64] -> row-major [R, K/2]; checks the padding bytes are zero."""
+    c_stage = np.asarray(c_stage, dtype=np.uint8)
+    G, R, _ = c_stage.shape
+    flat = c_stage.transpose(1, 0, 2).reshape(R, 64 * G)
+    assert not flat[:, kbytes:].any(), "code padding bytes must be zero"
+    return flat[:, :kbytes]
+
+
 def w_to_gpu(wc, ws):
-    """Upload an oracle-quantised weight (codes [O, K/2] or [E, O, K/2], row-major scales)."""
+    """Upload an oracle-quantised weight (row-major codes [O, K/2] and scales
+    [O, K/32], or stacks of them over experts) in the library's layout."""
     import activation_sparsity_fp4_amd as sq
     ws = np.asarray(ws)
+    wc = np.asarray(wc)
+    K = 2 * wc.shape[-1]
     if ws.ndim == 3:
-        return sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(np.stack([stage_major(x) for x in ws])))
-    return sq.MXFP4(u8_to_gpu(wc), u8_to_gpu(stage_major(ws)))
+        return sq.MXFP4(u8_to_gpu(np.stack([codes_stage_major(x) for x in wc])),
+                        u8_to_gpu(np.stack([stage_major(x) for x in ws])), K)
+    return sq.MXFP4(u8_to_gpu(codes_stage_major(wc)), u8_to_gpu(stage_major(ws)), K)
 
 
 def w_scales_rows(wq_scales, kblocks):
@@ -74,11 +98,18 @@ def w_scales_rows(wq_scales, kblocks):
     return row_major(to_np(wq_scales), kblocks)
 
 
+def w_codes_rows(wq_codes, kbytes):
+    """GPU weight codes [G, O, 64] -> row-major [O, K/2]."""
+    return codes_row_major(to_np(wq_codes), kbytes)
+
+
 def oracle_prepared(out):
     """Upload an oracle prepare result as the GPU's Prepared tuple."""
     import activation_sparsity_fp4_amd as sq
-    return sq.Prepared(u8_to_gpu(out["bb_codes"]), u8_to_gpu(stage_major(out["bb_scales"])),
-                       u8_to_gpu(out["res_codes"]), u8_to_gpu(stage_major(out["res_scales"])), None)
+    K = 2 * out["bb_codes"].shape[1]
+    return sq.Prepared(u8_to_gpu(codes_stage_major(out["bb_codes"])), u8_to_gpu(stage_major(out["bb_scales"])),
+                       u8_to_gpu(codes_stage_major(out["res_codes"])), u8_to_gpu(stage_major(out["res_scales"])),
+                       None, K)
 
 
 def assert_prepare_equal(got, want, rows=None):
@@ -90,6 +121,8 @@ def assert_prepare_equal(got, want, rows=None):
         g = to_np(g)
         if name.endswith("scales"):
             g = row_major(g, want[name].shape[1])
+        elif name.endswith("codes"):
+            g = codes_row_major(g, want[name].shape[1])
         if rows is not None:
             g = g[rows]
         w = want[name]

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 1
+    assert _lib.call("sharq_abi_version") == 2
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"

@@ -13,7 +13,7 @@ import pytest
 from oracle import linear_ref, prepare_ref, quantize_weight_ref
 from synth import bf16_round, workload_down_silu, workload_linear, workload_llama8b_mlp
 from gpu_util import (assert_prepare_equal, assert_y_close, bf16_to_gpu, oracle_prepared, to_np, u8_to_gpu,
-                      w_scales_rows, w_to_gpu)
+                      w_codes_rows, w_scales_rows, w_to_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,10 +59,10 @@ def test_linear_strided_output_and_zero_rows(sq):
     full = to_np(out.as_strided((T, O + 40), (O + 40, 1)))
     assert np.all(full[:, O:] == 7.0)  # padding columns untouched
     G = sq.stages(K)
-    e = sq.Prepared(torch.empty((0, K // 2), dtype=torch.uint8, device="cuda"),
+    e = sq.Prepared(torch.empty((G, 0, 64), dtype=torch.uint8, device="cuda"),
                     torch.empty((G, 0, 4), dtype=torch.uint8, device="cuda"),
-                    torch.empty((0, K // 2), dtype=torch.uint8, device="cuda"),
-                    torch.empty((G, 0, 4), dtype=torch.uint8, device="cuda"), None)
+                    torch.empty((G, 0, 64), dtype=torch.uint8, device="cuda"),
+                    torch.empty((G, 0, 4), dtype=torch.uint8, device="cuda"), None, K)
     y0 = sq.linear(e, w_to_gpu(wc, ws))
     assert y0.shape == (0, O)
 
@@ -98,7 +98,7 @@ def test_linear_128x4096_full(sq):
     prep = sq.prepare(bf16_to_gpu(wl["x"]), None, 2, 4)
     wq = sq.quantize_mxfp4(bf16_to_gpu(wl["w"]))
     assert_prepare_equal(prep, p)
-    assert np.array_equal(to_np(wq.codes), wc) and np.array_equal(w_scales_rows(wq.scales, ws.shape[1]), ws)
+    assert np.array_equal(w_codes_rows(wq.codes, wc.shape[1]), wc) and np.array_equal(w_scales_rows(wq.scales, ws.shape[1]), ws)
     y = sq.linear(prep, wq)
     y_ref, bound = linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
     assert_y_close(to_np(y), y_ref, bound)
@@ -112,7 +112,7 @@ def _sampled_linear_check(sq, x, gamma, n, m, w_bits, rows, cols):
     p = prepare_ref(x[rows], gamma, n, m)
     assert_prepare_equal(prep, p, rows=rows)
     wc, ws = quantize_weight_ref(w_bits[cols])
-    assert np.array_equal(to_np(wq.codes)[cols], wc)
+    assert np.array_equal(w_codes_rows(wq.codes, wc.shape[1])[cols], wc)
     assert np.array_equal(w_scales_rows(wq.scales, ws.shape[1])[cols], ws)
     y_ref, bound = linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
     assert_y_close(to_np(y)[np.ix_(rows, cols)], y_ref, bound)

@@ -12,7 +12,7 @@ import pytest
 from oracle import prepare_ref, quantize_weight_ref
 from synth import (adversarial_rows, bf16_round, bf16_to_f32, workload_down_silu, workload_linear,
                    workload_llama70b_decode, workload_llama8b_mlp, workload_qwen3_moe)
-from gpu_util import assert_prepare_equal, bf16_to_gpu, to_np, w_scales_rows
+from gpu_util import assert_prepare_equal, bf16_to_gpu, to_np, w_codes_rows, w_scales_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,7 @@ def test_prepare_strided_rows_single_block_and_no_mask(sq):
     assert_prepare_equal(sq.prepare(bf16_to_gpu(one), None, 8, 16), prepare_ref(one, None, 8, 16))
     # T = 0 is a no-op that returns empty outputs
     empty = sq.prepare(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"), None, 2, 4)
-    assert empty.bb_codes.shape == (0, 32) and empty.bb_scales.shape == (1, 0, 4)
+    assert empty.bb_codes.shape == (1, 0, 64) and empty.bb_scales.shape == (1, 0, 4)
 
 
 def test_prepare_deterministic(sq):
@@ -95,7 +95,7 @@ def test_prepare_deterministic(sq):
     xg = bf16_to_gpu(xb)
     a = sq.prepare(xg, None, 8, 16)
     b = sq.prepare(xg, None, 8, 16)
-    for f in a._fields:
+    for f in ("bb_codes", "bb_scales", "res_codes", "res_scales", "mask"):
         assert np.array_equal(to_np(getattr(a, f)), to_np(getattr(b, f)))
 
 
@@ -131,7 +131,7 @@ def test_quantize_exhaustive_bf16(sq):
     wc, ws = quantize_weight_ref(rows)
     got = sq.quantize_mxfp4(bf16_to_gpu(rows))
     assert np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
-    assert np.array_equal(to_np(got.codes), wc)
+    assert np.array_equal(w_codes_rows(got.codes, wc.shape[1]), wc)
 
 
 def test_quantize_weights_and_ragged(sq):
@@ -139,11 +139,11 @@ def test_quantize_weights_and_ragged(sq):
     w = workload_linear(T=8, K=4096, O=4096)["w"]
     wc, ws = quantize_weight_ref(w)
     got = sq.quantize_mxfp4(bf16_to_gpu(w))
-    assert np.array_equal(to_np(got.codes), wc) and np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
+    assert np.array_equal(w_codes_rows(got.codes, wc.shape[1]), wc) and np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
     xb = _mixed_input(33, 160, 3)
     wc, ws = quantize_weight_ref(xb)
     got = sq.quantize_mxfp4(bf16_to_gpu(xb))
-    assert np.array_equal(to_np(got.codes), wc) and np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
+    assert np.array_equal(w_codes_rows(got.codes, wc.shape[1]), wc) and np.array_equal(w_scales_rows(got.scales, ws.shape[1]), ws)
 
 
 def _rows_sample(T, count, seed):

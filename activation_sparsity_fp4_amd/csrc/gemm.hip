@@ -12,27 +12,26 @@
 // (FP4 x FP4, one E8M0 scale per lane per 32 K entries) on the SAME weight
 // fragment registers into the SAME fp32 accumulator.
 //
-// Tiling: a 256-thread workgroup computes a 128 (rows) x 256 (outputs) tile;
-// wave w covers rows 64*(w&1) .. +64 and outputs 128*(w>>1) .. +128, i.e. 2 x 4
-// MFMA tiles of 32 x 32. K advances 128 entries per stage (64 bytes of codes
-// per row per operand; with the stage-major layout of sharq_device.h one stage
-// of a tile is one contiguous run of every operand). A stage holds the backbone tile, the residual tile, the
-// weight tile and their scales (34 KB of LDS).
+// Tiling: a 256-thread workgroup is 2 x 2 waves; each wave computes WM x WN
+// MFMA tiles of 32 x 32, so the workgroup tile is (64 WM) x (64 WN). Two
+// shapes are built: 128 x 256 (WM = 2, WN = 4) and 256 x 256 (WM = WN = 4).
+// The activation side carries two operands (backbone and residual) against
+// one weight operand, so a tile twice as wide as it is tall balances the
+// bytes each stage loads. K advances 128 entries per stage (64 bytes of codes
+// per row per operand; with the stage-major layout of sharq_device.h one
+// stage of a tile is one contiguous run of every operand).
 //
-// Main path (K % 128 == 0): a ring of 4 LDS stages filled by buffer loads that
-// write straight into LDS (no register staging); four stages are in flight
-// ahead of the MFMAs, rows past the end of a matrix read as zero through the
-// buffer bounds check, and one barrier per stage recycles a slot as soon as
-// every wave holds that stage's fragments in registers. General
-// path (any K % 32 == 0): 2 LDS stages filled through registers.
+// Main path (K % 128 == 0): a ring of LDS stages (4 for 128 x 256, 3 for
+// 256 x 256) filled by buffer loads that write straight into LDS (no register
+// staging); all but one stage are in flight ahead of the MFMAs, rows past the
+// end of a matrix read as zero through the buffer bounds check, and one
+// barrier per stage recycles a slot as soon as every wave holds that stage's
+// fragments in registers. General path (any K % 32 == 0, 128 x 256 only):
+// 2 LDS stages filled through registers.
 //
 // LDS rows are 64 bytes; the 16-byte chunk c of row r sits at chunk position
 // c ^ ((r >> 2) & 3), which keeps the rows read by one MFMA fragment on
 // distinct banks of the 64-bank LDS.
-//
-// Codes and scales are stored stage-major (sharq_device.h): one stage of a
-// 128-row tile is a contiguous 8 KB run of codes and a 512-byte run of
-// scales, so every load uses whole cache lines.
 //
 // MFMA operand layouts (32x32x64, FP4): lane l holds row (l % 32) and the 32
 // consecutive K entries of block (l / 32) of the 64-entry K slice, low nibble
@@ -46,20 +45,37 @@
 namespace sharq {
 namespace {
 
-constexpr int kBM = 128;
-constexpr int kBN = 256;
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 64;  // 128 FP4 codes
-constexpr int kOffAs = 0;
-constexpr int kOffAr = kOffAs + kBM * kRowBytes;
-constexpr int kOffW = kOffAr + kBM * kRowBytes;
-constexpr int kOffSAs = kOffW + kBN * kRowBytes;
-constexpr int kOffSAr = kOffSAs + kBM * 4;
-constexpr int kOffSW = kOffSAr + kBM * 4;
-constexpr int kStage = kOffSW + kBN * 4;  // 34816 bytes
-constexpr int kRing = 4;                  // LDS stages of the main path
-constexpr int kLoadsPerStage = 10;        // buffer->LDS instructions per wave per stage
-constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past every bound: reads as 0
+constexpr int kRowBytes = 64;            // 128 FP4 codes
+constexpr int kLdsBytes = 160 * 1024;    // LDS of one CU
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every bound: reads as 0
+
+// Workgroup tile of 2 x 2 waves, each WM x WN MFMA tiles of 32 x 32, and the
+// layout of one LDS stage: backbone codes, residual codes, weight codes, then
+// the three scale runs (in that order, contiguous).
+template <int WM_, int WN_>
+struct Tile {
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int BM = 64 * WM, BN = 64 * WN;
+  static constexpr int kOffAs = 0;
+  static constexpr int kOffAr = BM * kRowBytes;
+  static constexpr int kOffW = 2 * BM * kRowBytes;
+  static constexpr int kOffSAs = kOffW + BN * kRowBytes;
+  static constexpr int kOffSAr = kOffSAs + BM * 4;
+  static constexpr int kOffSW = kOffSAr + BM * 4;
+  static constexpr int kStage = kOffSW + BN * 4;
+  static constexpr int kRing = kLdsBytes / kStage < 4 ? kLdsBytes / kStage : 4;
+  // buffer->LDS instructions per wave per stage: 1 KB code chunks of each
+  // activation operand, of the weight, and 256-byte scale runs (64 rows)
+  static constexpr int kAChunks = BM / 64;
+  static constexpr int kWChunks = BN / 64;
+  static constexpr int kSLoads = (2 * BM + BN) / 256;
+  static constexpr int kLoads = 2 * kAChunks + kWChunks + kSLoads;
+  static_assert((2 * BM + BN) % 256 == 0, "scale runs must split evenly over the four waves");
+  static_assert(kRing >= 3, "the ring keeps at least two stages in flight");
+};
+using SmallTile = Tile<2, 4>;  // 128 x 256, 34 KB stages, ring of 4
+using BigTile = Tile<4, 4>;    // 256 x 256, 51 KB stages, ring of 3
 
 // LDS chunk swizzle. gfx950 LDS has 64 four-byte banks; a ds_read_b128 of an
 // MFMA fragment serves 16 lanes (16 consecutive rows, one 16-byte chunk each)
@@ -71,51 +87,13 @@ __device__ __forceinline__ int swz(int row, int part) {
   return row * kRowBytes + ((part ^ swz_part(row)) << 4);
 }
 
+// An MFMA operand fragment from LDS. The FP4 form of the scaled MFMA reads
+// only the low 4 of its 8 operand registers, so the upper half is left
+// undefined (no registers are spent on it).
+typedef int v4i __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v8i frag(const uint8_t* p) {
-  const uint4 v = *reinterpret_cast<const uint4*>(p);
-  v8i r = {(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-  return r;
-}
-
-// One 64-entry K slice (SUB selects which half of the 128-entry stage).
-template <int SUB>
-__device__ __forceinline__ void compute_sub(const uint8_t* st, v16f (&acc)[2][4], int wm, int wn, int lr,
-                                            int lh, const uint32_t (&sa)[2][2], const uint32_t (&sw)[4]) {
-  v8i fa[2][2], fw[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 64 * wm + 32 * i + lr;
-    fa[0][i] = frag(st + kOffAs + swz(row, 2 * SUB + lh));
-    fa[1][i] = frag(st + kOffAr + swz(row, 2 * SUB + lh));
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) fw[j] = frag(st + kOffW + swz(128 * wn + 32 * j + lr, 2 * SUB + lh));
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[0][i], fw[j], acc[i][j], 4, 4, 2 * SUB,
-                                                                  (int)sa[0][i], 2 * SUB, (int)sw[j]);
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[1][i], fw[j], acc[i][j], 4, 4, 2 * SUB,
-                                                                  (int)sa[1][i], 2 * SUB, (int)sw[j]);
-    }
-}
-
-// All MFMAs of one 128-entry stage held in LDS at `st`.
-__device__ __forceinline__ void compute_stage(const uint8_t* st, v16f (&acc)[2][4], int wm, int wn, int lr,
-                                              int lh) {
-  uint32_t sa[2][2], sw[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 64 * wm + 32 * i + lr;
-    sa[0][i] = *reinterpret_cast<const uint32_t*>(st + kOffSAs + 4 * row) >> (8 * lh);
-    sa[1][i] = *reinterpret_cast<const uint32_t*>(st + kOffSAr + 4 * row) >> (8 * lh);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    sw[j] = *reinterpret_cast<const uint32_t*>(st + kOffSW + 4 * (128 * wn + 32 * j + lr)) >> (8 * lh);
-  compute_sub<0>(st, acc, wm, wn, lr, lh, sa, sw);
-  compute_sub<1>(st, acc, wm, wn, lr, lh, sa, sw);
+  const v4i v = *reinterpret_cast<const v4i*>(p);
+  return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
 }
 
 struct Operands {
@@ -132,7 +110,7 @@ struct Operands {
 // Row sources of one output tile: which activation row feeds tile row r, or -1.
 struct TileRows {
   int64_t m0;          // first output row of the tile
-  int64_t rows_valid;  // output rows of the tile that exist (<= kBM)
+  int64_t rows_valid;  // output rows of the tile that exist (<= the tile height)
   const int32_t* gather;  // activation row of each output row, or nullptr (identity)
   __device__ __forceinline__ int64_t src(int r) const {
     if (r >= rows_valid) return -1;
@@ -141,8 +119,62 @@ struct TileRows {
   }
 };
 
+// Fragments and scale dwords of one 64-entry sub-step, held in registers.
+template <class C>
+struct Frags {
+  v8i a[2][C::WM];  // [path][row block]
+  v8i w[C::WN];
+};
+template <class C>
+struct Scales {
+  uint32_t a[2][C::WM];  // [path][row block]
+  uint32_t w[C::WN];
+};
+
+template <class C, int SUB>
+__device__ __forceinline__ void read_frags(const uint8_t* st, Frags<C>& f, int wm, int wn, int lr, int lh) {
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) {
+    const int row = 32 * C::WM * wm + 32 * i + lr;
+    f.a[0][i] = frag(st + C::kOffAs + swz(row, 2 * SUB + lh));
+    f.a[1][i] = frag(st + C::kOffAr + swz(row, 2 * SUB + lh));
+  }
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j)
+    f.w[j] = frag(st + C::kOffW + swz(32 * C::WN * wn + 32 * j + lr, 2 * SUB + lh));
+}
+
+// The scale dword of a lane's row holds the bytes of the stage's 4 blocks;
+// shifted right by 8 * (lane / 32), byte 0 (sub-step 0) and byte 2 (sub-step
+// 1) are the blocks of that lane's K half, picked by the MFMA's op_sel.
+template <class C>
+__device__ __forceinline__ void read_scales(const uint8_t* st, Scales<C>& c, int wm, int wn, int lr, int lh) {
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) {
+    const int row = 32 * C::WM * wm + 32 * i + lr;
+    c.a[0][i] = *reinterpret_cast<const uint32_t*>(st + C::kOffSAs + 4 * row) >> (8 * lh);
+    c.a[1][i] = *reinterpret_cast<const uint32_t*>(st + C::kOffSAr + 4 * row) >> (8 * lh);
+  }
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j)
+    c.w[j] = *reinterpret_cast<const uint32_t*>(st + C::kOffSW + 4 * (32 * C::WN * wn + 32 * j + lr)) >> (8 * lh);
+}
+
+template <class C, int SUB>
+__device__ __forceinline__ void mfma_sub(const Frags<C>& f, const Scales<C>& c, v16f (&acc)[C::WM][C::WN]) {
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[0][i], f.w[j], acc[i][j], 4, 4, 2 * SUB,
+                                                                  (int)c.a[0][i], 2 * SUB, (int)c.w[j]);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[1][i], f.w[j], acc[i][j], 4, 4, 2 * SUB,
+                                                                  (int)c.a[1][i], 2 * SUB, (int)c.w[j]);
+    }
+}
+
 // ---------------------------------------------------------------------------
-// Main path: buffer loads straight into a 4-stage LDS ring.
+// Main path: buffer loads straight into a ring of LDS stages.
 // ---------------------------------------------------------------------------
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -175,16 +207,19 @@ __device__ __forceinline__ void buffer_to_lds4(i32x4 rsrc, uint32_t voff, uint32
                :: "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
 }
 
+template <class C>
 struct RingLoader {
-  i32x4 a_codes[2], a_scales[2], w_codes, w_scales;
-  uint32_t a_off[2];   // byte offset of this lane's A code chunk inside a stage (chunks j = 0, 1), kOOB if absent
-  uint32_t w_off[4];   // same for the 4 W chunks
-  uint32_t s_off[2];   // scale-row byte offsets for this wave's two scale instructions
-  int wave;            // wave-uniform
+  i32x4 a_codes[2], w_codes;
+  i32x4 s_rsrc[C::kSLoads];     // tensor of each scale run this wave loads
+  uint32_t a_off[C::kAChunks];  // byte offset of this lane's A code chunk inside a stage, kOOB if absent
+  uint32_t w_off[C::kWChunks];  // same for the W chunks
+  uint32_t s_off[C::kSLoads];   // this lane's scale-row offset inside a stage, kOOB if absent
+  bool s_is_w[C::kSLoads];      // wave-uniform: the scale run belongs to W
+  int wave;                     // wave-uniform
   int nsteps;
   uint32_t a_stage_bytes, w_stage_bytes;  // scale bytes of one stage: 4 per row (codes: 64 per row)
 
-  // Issue the 10 loads of stage s (K entries [128 s, 128 s + 128)) into `st`.
+  // Issue the loads of stage s (K entries [128 s, 128 s + 128)) into `st`.
   // Past the last stage every offset is moved out of range: the loads keep
   // the per-stage instruction count constant and read nothing.
   __device__ __forceinline__ void issue(uint8_t* st, int s) const {
@@ -193,23 +228,23 @@ struct RingLoader {
     const uint32_t ka = live ? (uint32_t)s * a_stage_bytes * 16 : kOOB;  // stage start in the code arrays
     const uint32_t kw = live ? (uint32_t)s * w_stage_bytes * 16 : kOOB;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int chunk = wave + 4 * j;  // 1 KB chunk inside the 8 KB A tile
-      buffer_to_lds16(a_codes[0], a_off[j] + ka, base + kOffAs + 1024 * chunk);
-      buffer_to_lds16(a_codes[1], a_off[j] + ka, base + kOffAr + 1024 * chunk);
+    for (int j = 0; j < C::kAChunks; ++j) {
+      const int chunk = wave + 4 * j;  // 1 KB chunk (16 rows) of the activation tile
+      buffer_to_lds16(a_codes[0], a_off[j] + ka, base + C::kOffAs + 1024 * chunk);
+      buffer_to_lds16(a_codes[1], a_off[j] + ka, base + C::kOffAr + 1024 * chunk);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int chunk = wave + 4 * j;  // 1 KB chunk inside the 16 KB W tile
-      buffer_to_lds16(w_codes, w_off[j] + kw, base + kOffW + 1024 * chunk);
+    for (int j = 0; j < C::kWChunks; ++j) {
+      const int chunk = wave + 4 * j;  // 1 KB chunk (16 rows) of the weight tile
+      buffer_to_lds16(w_codes, w_off[j] + kw, base + C::kOffW + 1024 * chunk);
     }
     const uint32_t ksa = live ? (uint32_t)s * a_stage_bytes : kOOB;
     const uint32_t ksw = live ? (uint32_t)s * w_stage_bytes : kOOB;
-    // scale rows: waves 0,1 -> backbone rows 64w..; waves 2,3 -> residual rows; then W rows 64w..
-    const i32x4 ars = wave < 2 ? a_scales[0] : a_scales[1];
-    const uint32_t aoff = (wave < 2 ? kOffSAs : kOffSAr) + 256 * (wave & 1);
-    buffer_to_lds4(ars, s_off[0] + ksa, base + aoff);
-    buffer_to_lds4(w_scales, s_off[1] + ksw, base + kOffSW + 256 * wave);
+#pragma unroll
+    for (int i = 0; i < C::kSLoads; ++i) {
+      const int q = wave + 4 * i;  // 64-row run q of the concatenated [As | Ar | W] scale rows
+      buffer_to_lds4(s_rsrc[i], s_off[i] + (s_is_w[i] ? ksw : ksa), base + C::kOffSAs + 256 * q);
+    }
   }
 };
 
@@ -228,94 +263,49 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Each ring stage is its own __shared__ object so that the compiler's wait
-// insertion can tell a read of one stage from the loads still filling another.
-struct RingStages {
-  uint8_t* st[kRing];
-};
-
-// Fragments and scale dwords of one 64-entry sub-step, held in registers.
-struct Frags {
-  v8i a[2][2];  // [path][row block]
-  v8i w[4];
-};
-struct Scales {
-  uint32_t a[2][2];  // [path][row block]
-  uint32_t w[4];
-};
-
-template <int SUB>
-__device__ __forceinline__ void read_frags(const uint8_t* st, Frags& f, int wm, int wn, int lr, int lh) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 64 * wm + 32 * i + lr;
-    f.a[0][i] = frag(st + kOffAs + swz(row, 2 * SUB + lh));
-    f.a[1][i] = frag(st + kOffAr + swz(row, 2 * SUB + lh));
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.w[j] = frag(st + kOffW + swz(128 * wn + 32 * j + lr, 2 * SUB + lh));
-}
-
-__device__ __forceinline__ void read_scales(const uint8_t* st, Scales& c, int wm, int wn, int lr, int lh) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 64 * wm + 32 * i + lr;
-    c.a[0][i] = *reinterpret_cast<const uint32_t*>(st + kOffSAs + 4 * row) >> (8 * lh);
-    c.a[1][i] = *reinterpret_cast<const uint32_t*>(st + kOffSAr + 4 * row) >> (8 * lh);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    c.w[j] = *reinterpret_cast<const uint32_t*>(st + kOffSW + 4 * (128 * wn + 32 * j + lr)) >> (8 * lh);
-}
-
-template <int SUB>
-__device__ __forceinline__ void mfma_sub(const Frags& f, const Scales& c, v16f (&acc)[2][4]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[0][i], f.w[j], acc[i][j], 4, 4, 2 * SUB,
-                                                                  (int)c.a[0][i], 2 * SUB, (int)c.w[j]);
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[1][i], f.w[j], acc[i][j], 4, 4, 2 * SUB,
-                                                                  (int)c.a[1][i], 2 * SUB, (int)c.w[j]);
-    }
-}
-
-// Iteration s of the ring (slot I = s % 4). On entry f0 / c hold sub-step 0
-// of stage s. The sub-step 1 reads are issued before the sub-step 0 MFMAs;
-// the barrier that makes stage s+1 visible sits between the two MFMA groups,
-// and the sub-step 0 reads of stage s+1 are issued before the sub-step 1
-// MFMAs, so LDS latency hides behind 16 MFMAs each time. Once every wave has
-// its stage-s fragments in registers (the barrier waits on lgkmcnt), slot I
-// is refilled with stage s+4: four stages are in flight. Every iteration has
-// the same shape (batches past the last stage are issued with out-of-range
-// offsets and read nothing), so the vmcnt bound is a constant and no branch
-// splits the MFMA groups from the barrier.
-template <int I>
-__device__ __forceinline__ void ring_iter(const RingLoader& ld, const RingStages& rs, int s, Frags& f0, Frags& f1,
-                                          Scales& c, Scales& cn, v16f (&acc)[2][4], int wm, int wn, int lr, int lh) {
-  read_frags<1>(rs.st[I], f1, wm, wn, lr, lh);
-  mfma_sub<0>(f0, c, acc);
-  // schedule: the 8 fragment reads first, then the 16 MFMAs
-  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+// Iteration s of the ring: `cur` holds stage s, `next` stage s+1. On entry
+// f0 / c hold sub-step 0 of stage s. The sub-step 1 reads are issued before
+// the sub-step 0 MFMAs; the barrier that makes stage s+1 visible sits between
+// the two MFMA groups, and the sub-step 0 reads of stage s+1 are issued
+// before the sub-step 1 MFMAs, so LDS latency hides behind the MFMAs each
+// time. Once every wave has its stage-s fragments in registers (the barrier
+// waits on lgkmcnt), the slot of stage s is refilled with stage s+kRing.
+// Every iteration has the same shape (batches past the last stage are issued
+// with out-of-range offsets and read nothing), so the vmcnt bound is a
+// constant and no branch splits the MFMA groups from the barrier.
+template <class C>
+__device__ __forceinline__ void ring_iter(const RingLoader<C>& ld, uint8_t* cur, const uint8_t* next, int s,
+                                          Frags<C>& f0, Frags<C>& f1, Scales<C>& c, Scales<C>& cn,
+                                          v16f (&acc)[C::WM][C::WN], int wm, int wn, int lr, int lh) {
+  constexpr int kReads = 2 * C::WM + C::WN;   // fragment reads of a sub-step
+  constexpr int kMfma = 2 * C::WM * C::WN;    // MFMAs of a sub-step
+  read_frags<C, 1>(cur, f1, wm, wn, lr, lh);
+  mfma_sub<C, 0>(f0, c, acc);
+  // schedule: the fragment reads first, then the MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<2 * kLoadsPerStage>();  // batch s+1 landed; s+2, s+3 may be in flight
+  wait_vmcnt<(C::kRing - 2) * C::kLoads>();  // batch s+1 landed; later batches may be in flight
   ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  ld.issue(rs.st[I], s + kRing);
-  read_scales(rs.st[(I + 1) % kRing], cn, wm, wn, lr, lh);
-  read_frags<0>(rs.st[(I + 1) % kRing], f0, wm, wn, lr, lh);
-  mfma_sub<1>(f1, c, acc);
-  // schedule: all LDS reads of stage s+1 first, then the 16 MFMAs
-  __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  ld.issue(cur, s + C::kRing);
+  read_scales<C>(next, cn, wm, wn, lr, lh);
+  read_frags<C, 0>(next, f0, wm, wn, lr, lh);
+  mfma_sub<C, 1>(f1, c, acc);
+  // schedule: all LDS reads of stage s+1 first, then the MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReads, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
   __builtin_amdgcn_sched_barrier(0);
   c = cn;
 }
 
-__device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows& tr, int64_t n0,
-                                              const RingStages& rs, v16f (&acc)[2][4]) {
+// The ring's stages sit back to back in one LDS array, kStage bytes apart.
+// The loop is kept rolled (the slot is a uniform runtime index): unrolling it
+// by the ring length makes the register allocator rotate fragment registers
+// between copies and, at 256 accumulators, spill.
+template <class C>
+__device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows& tr, int64_t n0, uint8_t* ring,
+                                              v16f (&acc)[C::WM][C::WN]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -323,62 +313,76 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t G = op.nsteps;
 
-  RingLoader ld;
+  RingLoader<C> ld;
   ld.wave = wave;
   ld.a_codes[0] = make_rsrc(op.a_codes[0], op.a_rows_total * G * kRowBytes);
   ld.a_codes[1] = make_rsrc(op.a_codes[1], op.a_rows_total * G * kRowBytes);
-  ld.a_scales[0] = make_rsrc(op.a_scales[0], op.a_rows_total * G * 4);
-  ld.a_scales[1] = make_rsrc(op.a_scales[1], op.a_rows_total * G * 4);
   ld.w_codes = make_rsrc(op.w_codes, op.O * G * kRowBytes);
-  ld.w_scales = make_rsrc(op.w_scales, op.O * G * 4);
+  const i32x4 as_rsrc0 = make_rsrc(op.a_scales[0], op.a_rows_total * G * 4);
+  const i32x4 as_rsrc1 = make_rsrc(op.a_scales[1], op.a_rows_total * G * 4);
+  const i32x4 ws_rsrc = make_rsrc(op.w_scales, op.O * G * 4);
   ld.a_stage_bytes = (uint32_t)(op.a_rows_total * 4);
   ld.w_stage_bytes = (uint32_t)(op.O * 4);
   // The LDS chunk position a lane fills is fixed (lane * 16 inside its 1 KB
   // chunk); pick the global 16-byte chunk that belongs there after the swizzle.
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < C::kAChunks; ++j) {
     const int row = 16 * (wave + 4 * j) + (lane >> 2);
     const int part = (lane & 3) ^ swz_part(row);
     const int64_t src = tr.src(row);
     ld.a_off[j] = src >= 0 ? (uint32_t)(src * kRowBytes + part * 16) : kOOB;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < C::kWChunks; ++j) {
     const int row = 16 * (wave + 4 * j) + (lane >> 2);
     const int part = (lane & 3) ^ swz_part(row);
     const int64_t o = n0 + row;
     ld.w_off[j] = o < op.O ? (uint32_t)(o * kRowBytes + part * 16) : kOOB;
   }
-  {
-    const int64_t src = tr.src(64 * (wave & 1) + lane);
-    ld.s_off[0] = src >= 0 ? (uint32_t)(src * 4) : kOOB;
-    const int64_t o = n0 + 64 * wave + lane;
-    ld.s_off[1] = o < op.O ? (uint32_t)(o * 4) : kOOB;
+  // scale runs: 64-row run q of [backbone rows | residual rows | weight rows]
+#pragma unroll
+  for (int i = 0; i < C::kSLoads; ++i) {
+    const int q = wave + 4 * i;
+    constexpr int qa = C::BM / 64;
+    if (q < 2 * qa) {
+      const int64_t src = tr.src(64 * (q % qa) + lane);
+      ld.s_rsrc[i] = q < qa ? as_rsrc0 : as_rsrc1;
+      ld.s_off[i] = src >= 0 ? (uint32_t)(src * 4) : kOOB;
+      ld.s_is_w[i] = false;
+    } else {
+      const int64_t o = n0 + 64 * (q - 2 * qa) + lane;
+      ld.s_rsrc[i] = ws_rsrc;
+      ld.s_off[i] = o < op.O ? (uint32_t)(o * 4) : kOOB;
+      ld.s_is_w[i] = true;
+    }
   }
 
   const int nsteps = op.nsteps;
   ld.nsteps = nsteps;
-  static_assert(kRing == 4, "the iteration sequence below is unrolled for 4 stages");
 #pragma unroll
-  for (int b = 0; b < kRing; ++b) ld.issue(rs.st[b], b);
-  wait_vmcnt<3 * kLoadsPerStage>();  // batch 0 landed
+  for (int b = 0; b < C::kRing; ++b) ld.issue(ring + b * C::kStage, b);
+  wait_vmcnt<(C::kRing - 1) * C::kLoads>();  // batch 0 landed
   ring_barrier();
-  Frags f0, f1;
-  Scales c, cn;
-  read_scales(rs.st[0], c, wm, wn, lr, lh);
-  read_frags<0>(rs.st[0], f0, wm, wn, lr, lh);
-  for (int s = 0; s < nsteps; s += kRing) {
-    ring_iter<0>(ld, rs, s, f0, f1, c, cn, acc, wm, wn, lr, lh);
-    if (s + 1 < nsteps) ring_iter<1>(ld, rs, s + 1, f0, f1, c, cn, acc, wm, wn, lr, lh);
-    if (s + 2 < nsteps) ring_iter<2>(ld, rs, s + 2, f0, f1, c, cn, acc, wm, wn, lr, lh);
-    if (s + 3 < nsteps) ring_iter<3>(ld, rs, s + 3, f0, f1, c, cn, acc, wm, wn, lr, lh);
+  Frags<C> f0, f1;
+  Scales<C> c, cn;
+  read_scales<C>(ring, c, wm, wn, lr, lh);
+  read_frags<C, 0>(ring, f0, wm, wn, lr, lh);
+  int slot = 0;
+#pragma unroll 1
+  for (int s = 0; s < nsteps; ++s) {
+    const int nslot = slot + 1 == C::kRing ? 0 : slot + 1;
+    ring_iter<C>(ld, ring + slot * C::kStage, ring + nslot * C::kStage, s, f0, f1, c, cn, acc, wm, wn, lr, lh);
+    slot = nslot;
   }
   wait_vmcnt<0>();  // drain the trailing out-of-range batches before the LDS is reused
 }
 
 // ---------------------------------------------------------------------------
-// General path (K % 128 != 0): two LDS stages staged through registers.
+// General path (K % 128 != 0): two LDS stages staged through registers, on
+// the 128 x 256 tile.
 // ---------------------------------------------------------------------------
+
+using RegTile = SmallTile;
 
 struct Prefetch {
   uint4 a[2][2];  // [path][chunk]
@@ -389,7 +393,7 @@ struct Prefetch {
 
 // The scale dword of (stage s, row) in the stage-major layout; bytes of a
 // last, partial stage past the row's blocks are masked to zero (their codes
-// are zero too).
+// are not read either).
 __device__ __forceinline__ uint32_t load_scales4(const uint8_t* scales, int64_t row, int64_t rows, int64_t s,
                                                  int64_t kblocks) {
   uint32_t v = *reinterpret_cast<const uint32_t*>(scales + s * rows * 4 + row * 4);
@@ -436,17 +440,17 @@ __device__ __forceinline__ void store_stage_regs(const Prefetch& pf, uint8_t* st
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int row = r0 + 64 * c;
-    *reinterpret_cast<uint4*>(st + kOffAs + swz(row, part)) = pf.a[0][c];
-    *reinterpret_cast<uint4*>(st + kOffAr + swz(row, part)) = pf.a[1][c];
+    *reinterpret_cast<uint4*>(st + RegTile::kOffAs + swz(row, part)) = pf.a[0][c];
+    *reinterpret_cast<uint4*>(st + RegTile::kOffAr + swz(row, part)) = pf.a[1][c];
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(st + kOffW + swz(r0 + 64 * c, part)) = pf.w[c];
-  *reinterpret_cast<uint32_t*>(st + ((tid >> 7) ? kOffSAr : kOffSAs) + 4 * (tid & 127)) = pf.sa;
-  *reinterpret_cast<uint32_t*>(st + kOffSW + 4 * tid) = pf.sw;
+  for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(st + RegTile::kOffW + swz(r0 + 64 * c, part)) = pf.w[c];
+  *reinterpret_cast<uint32_t*>(st + ((tid >> 7) ? RegTile::kOffSAr : RegTile::kOffSAs) + 4 * (tid & 127)) = pf.sa;
+  *reinterpret_cast<uint32_t*>(st + RegTile::kOffSW + 4 * tid) = pf.sw;
 }
 
 __device__ __forceinline__ void mainloop_regs(const Operands& op, const TileRows& tr, int64_t n0, uint8_t* buf0,
-                                              uint8_t* buf1, v16f (&acc)[2][4]) {
+                                              uint8_t* buf1, v16f (&acc)[RegTile::WM][RegTile::WN]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -471,7 +475,13 @@ __device__ __forceinline__ void mainloop_regs(const Operands& op, const TileRows
     const uint8_t* cur = (s & 1) ? buf1 : buf0;
     const bool more = s + 1 < op.nsteps;
     if (more) load_stage_regs(pf, op, s + 1, tid, a_src, a_src_scale, w_row, w_row_scale);
-    compute_stage(cur, acc, wm, wn, lr, lh);
+    Frags<RegTile> f;
+    Scales<RegTile> c;
+    read_scales<RegTile>(cur, c, wm, wn, lr, lh);
+    read_frags<RegTile, 0>(cur, f, wm, wn, lr, lh);
+    mfma_sub<RegTile, 0>(f, c, acc);
+    read_frags<RegTile, 1>(cur, f, wm, wn, lr, lh);
+    mfma_sub<RegTile, 1>(f, c, acc);
     if (more) store_stage_regs(pf, (s & 1) ? buf0 : buf1, tid);
     __syncthreads();
   }
@@ -481,48 +491,58 @@ __device__ __forceinline__ void mainloop_regs(const Operands& op, const TileRows
 // Kernels
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void zero_acc(v16f (&acc)[2][4]) {
+template <class C>
+__device__ __forceinline__ void zero_acc(v16f (&acc)[C::WM][C::WN]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < C::WN; ++j) acc[i][j] = v16f{};
 }
 
-// Store the tile: output row m0 + r (r < rows_valid) of y with leading dimension ldy.
-__device__ __forceinline__ void store_tile(const v16f (&acc)[2][4], float* __restrict__ y, int64_t ldy, int64_t m0,
-                                           int64_t rows_valid, int64_t n0, int64_t O) {
+// Store the tile: output row m0 + r (r < rows_valid) of y with leading
+// dimension ldy. Each MFMA tile is stored on its own (the scheduling barrier
+// keeps the compiler from moving every accumulator into VGPRs at once); a
+// tile that lies wholly inside Y skips the per-element bounds checks.
+template <class C>
+__device__ __forceinline__ void store_tile(const v16f (&acc)[C::WM][C::WN], float* __restrict__ y, int64_t ldy,
+                                           int64_t m0, int64_t rows_valid, int64_t n0, int64_t O) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 31, lh = lane >> 5;
+  const bool full = rows_valid == C::BM && n0 + C::BN <= O;
+  float* base = y + (m0 + 32 * C::WM * wm + 4 * lh) * ldy + n0 + 32 * C::WN * wn + lr;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t o = n0 + 128 * wn + 32 * j + lr;
+    for (int j = 0; j < C::WN; ++j) {
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (rr < rows_valid && o < O) y[(m0 + rr) * ldy + o] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r)
+          base[(32 * i + 8 * (r >> 2) + (r & 3)) * ldy + 32 * j] = acc[i][j][r];
+      } else {
+        const int64_t o = n0 + 32 * C::WN * wn + 32 * j + lr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 32 * C::WM * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (rr < rows_valid && o < O) y[(m0 + rr) * ldy + o] = acc[i][j][r];
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 }
+
+// LDS of the main loops: the ring's stages, or the general path's double buffer.
+#define SHARQ_GEMM_LDS(C, kRingPath) \
+  __shared__ __attribute__((aligned(16))) uint8_t lds[(kRingPath ? C::kRing : 2) * C::kStage];
 
 // Plain two-path GEMM. Tiles are assigned so that each XCD (workgroups are
 // dispatched round-robin over 8 XCDs) receives a contiguous range of tiles;
 // inside a range consecutive tiles share a weight column tile.
-// LDS of the main loops: the ring path uses four stage objects, the general
-// path the first two as one contiguous double buffer.
-#define SHARQ_GEMM_LDS                                                                    \
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s0[kStage];                         \
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s1[kStage];                         \
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s2[kRingPath ? kStage : 16];        \
-  __shared__ __attribute__((aligned(16))) uint8_t lds_s3[kRingPath ? kStage : 16];
-
-template <bool kRingPath>
+template <class C, bool kRingPath>
 __global__ __launch_bounds__(kThreads) void linear_kernel(Operands op, int64_t T, float* __restrict__ y,
                                                           int64_t ldy, int tiles_m, int tiles_total) {
-  SHARQ_GEMM_LDS
+  SHARQ_GEMM_LDS(C, kRingPath)
   int tile = blockIdx.x;
   if ((tiles_total & 7) == 0) {
     const int per_xcd = tiles_total >> 3;
@@ -530,17 +550,17 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(Operands op, int64_t T
   }
   const int tm = tile % tiles_m, tn = tile / tiles_m;
   TileRows tr;
-  tr.m0 = (int64_t)tm * kBM;
-  tr.rows_valid = T - tr.m0 < kBM ? T - tr.m0 : kBM;
+  tr.m0 = (int64_t)tm * C::BM;
+  tr.rows_valid = T - tr.m0 < C::BM ? T - tr.m0 : C::BM;
   tr.gather = nullptr;
-  const int64_t n0 = (int64_t)tn * kBN;
-  v16f acc[2][4];
-  zero_acc(acc);
+  const int64_t n0 = (int64_t)tn * C::BN;
+  v16f acc[C::WM][C::WN];
+  zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring(op, tr, n0, RingStages{{lds_s0, lds_s1, lds_s2, lds_s3}}, acc);
+    mainloop_ring<C>(op, tr, n0, lds, acc);
   else
-    mainloop_regs(op, tr, n0, lds_s0, lds_s1, acc);
-  store_tile(acc, y, ldy, tr.m0, tr.rows_valid, n0, op.O);
+    mainloop_regs(op, tr, n0, lds, lds + C::kStage, acc);
+  store_tile<C>(acc, y, ldy, tr.m0, tr.rows_valid, n0, op.O);
 }
 
 // Inclusive prefix sum across a 64-lane wave.
@@ -553,14 +573,16 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// Grouped two-path GEMM over token-sorted expert segments. blockIdx.y is a
-// linear index over all (expert, row-tile) pairs; the expert is found by a
-// prefix sum of per-expert tile counts. blockIdx.x is the output column tile.
+// Grouped two-path GEMM over token-sorted expert segments (128 x 256 tiles).
+// blockIdx.y is a linear index over all (expert, row-tile) pairs; the expert
+// is found by a prefix sum of per-expert tile counts. blockIdx.x is the output
+// column tile.
 template <bool kRingPath>
 __global__ __launch_bounds__(kThreads) void linear_grouped_kernel(
     Operands op, const int32_t* __restrict__ a_rows, const int32_t* __restrict__ seg, int E,
     const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, float* __restrict__ y) {
-  SHARQ_GEMM_LDS
+  using C = SmallTile;
+  SHARQ_GEMM_LDS(C, kRingPath)
   __shared__ int s_info[2];
   const int tid = threadIdx.x;
   const int target = blockIdx.y;
@@ -571,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void linear_grouped_kernel(
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + tid;
       const int cnt = e < E ? seg[e + 1] - seg[e] : 0;
-      const int tiles = (cnt + kBM - 1) / kBM;
+      const int tiles = (cnt + C::BM - 1) / C::BM;
       const int incl = wave_inclusive_scan(tiles, tid);
       const int excl = incl - tiles;
       if (e < E && target >= base + excl && target < base + incl) {
@@ -585,20 +607,20 @@ __global__ __launch_bounds__(kThreads) void linear_grouped_kernel(
   const int e = s_info[0];
   if (e < 0) return;  // uniform across the workgroup
   TileRows tr;
-  tr.m0 = seg[e] + (int64_t)s_info[1] * kBM;
+  tr.m0 = seg[e] + (int64_t)s_info[1] * C::BM;
   const int64_t hi = seg[e + 1];
-  tr.rows_valid = hi - tr.m0 < kBM ? hi - tr.m0 : kBM;
+  tr.rows_valid = hi - tr.m0 < C::BM ? hi - tr.m0 : C::BM;
   tr.gather = a_rows;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t n0 = (int64_t)blockIdx.x * C::BN;
   op.w_codes = w_codes_all + (int64_t)e * op.O * kRowBytes * op.nsteps;  // [E][G][O][64]
   op.w_scales = w_scales_all + (int64_t)e * op.O * 4 * op.nsteps;          // [E][G][O][4]
-  v16f acc[2][4];
-  zero_acc(acc);
+  v16f acc[C::WM][C::WN];
+  zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring(op, tr, n0, RingStages{{lds_s0, lds_s1, lds_s2, lds_s3}}, acc);
+    mainloop_ring<C>(op, tr, n0, lds, acc);
   else
-    mainloop_regs(op, tr, n0, lds_s0, lds_s1, acc);
-  store_tile(acc, y, op.O, tr.m0, tr.rows_valid, n0, op.O);
+    mainloop_regs(op, tr, n0, lds, lds + C::kStage, acc);
+  store_tile<C>(acc, y, op.O, tr.m0, tr.rows_valid, n0, op.O);
 }
 
 Operands make_operands(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
@@ -624,19 +646,34 @@ bool ring_path_ok(int64_t rows, int64_t O, int64_t K) {
   return K % 128 == 0 && rows * (K / 2) < lim && O * (K / 2) < lim;
 }
 
+template <class C, bool kRingPath>
+void launch_tiles(const Operands& op, int64_t T, float* y, int64_t ldy, hipStream_t stream) {
+  const int tiles_m = (int)((T + C::BM - 1) / C::BM);
+  const int tiles_n = (int)((op.O + C::BN - 1) / C::BN);
+  const int total = tiles_m * tiles_n;
+  hipLaunchKernelGGL((linear_kernel<C, kRingPath>), dim3(total), dim3(kThreads), 0, stream, op, T, y, ldy, tiles_m,
+                     total);
+}
+
+// 256 x 256 tiles need this many tiles to keep every CU busy for a few
+// rounds; below it the 128 x 256 tile spreads the work over more CUs.
+constexpr int64_t kBigTileMin = 768;
+
 }  // namespace
 
 hipError_t launch_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
                          const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                          int64_t T, int64_t O, int64_t K, float* y, int64_t ldy, hipStream_t stream) {
   const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K);
-  const int tiles_m = (int)((T + kBM - 1) / kBM);
-  const int tiles_n = (int)((O + kBN - 1) / kBN);
-  const int total = tiles_m * tiles_n;
-  if (ring_path_ok(T, O, K))
-    hipLaunchKernelGGL(linear_kernel<true>, dim3(total), dim3(kThreads), 0, stream, op, T, y, ldy, tiles_m, total);
-  else
-    hipLaunchKernelGGL(linear_kernel<false>, dim3(total), dim3(kThreads), 0, stream, op, T, y, ldy, tiles_m, total);
+  if (!ring_path_ok(T, O, K)) {
+    launch_tiles<SmallTile, false>(op, T, y, ldy, stream);
+  } else {
+    const int64_t big = ((T + BigTile::BM - 1) / BigTile::BM) * ((O + BigTile::BN - 1) / BigTile::BN);
+    if (big >= kBigTileMin)
+      launch_tiles<BigTile, true>(op, T, y, ldy, stream);
+    else
+      launch_tiles<SmallTile, true>(op, T, y, ldy, stream);
+  }
   return hipGetLastError();
 }
 
@@ -648,8 +685,8 @@ hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scal
   const Operands op =
       make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, a_rows_total, O, K);
   // every expert contributes ceil(count / 128) row tiles: at most P/128 + E in total
-  const int64_t tiles_m_bound = (P + kBM - 1) / kBM + E;
-  const int tiles_n = (int)((O + kBN - 1) / kBN);
+  const int64_t tiles_m_bound = (P + SmallTile::BM - 1) / SmallTile::BM + E;
+  const int tiles_n = (int)((O + SmallTile::BN - 1) / SmallTile::BN);
   const dim3 grid(tiles_n, (unsigned)tiles_m_bound);
   if (ring_path_ok(a_rows_total, O, K))
     hipLaunchKernelGGL(linear_grouped_kernel<true>, grid, dim3(kThreads), 0, stream, op, a_rows, seg_offsets, E,
@@ -661,4 +698,3 @@ hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scal
 }
 
 }  // namespace sharq
-

@@ -134,3 +134,18 @@ def test_down_proj_full_size(sq, n, m):
     print(f"linear workload down 2048x14336 -> 4096 {n}:{m}", flush=True)
     wl = workload_down_silu()
     _sampled_linear_check(sq, wl["x"], None, n, m, wl["w"], _sample(2048, 48, 3), _sample(4096, 384, 4))
+
+
+def test_linear_big_tile_ragged(sq):
+    # enough 256 x 256 tiles for the large-tile kernel, with a ragged last row
+    # tile (2 rows) and a ragged last column tile; sampled rows and columns
+    # include both edges
+    print("linear 256x256 tiles, ragged: 2050 x 1024 -> 22000", flush=True)
+    T, K, O = 2050, 1024, 22000
+    rng = np.random.default_rng(77)
+    x = (rng.standard_normal((T, K)) * rng.lognormal(0, 0.5, (T, 1))).astype(np.float32)
+    x[:, rng.choice(K, 8, replace=False)] *= 50
+    w = (rng.standard_normal((O, K)) * 0.02).astype(np.float32)
+    rows = np.unique(np.concatenate([_sample(T, 40, 5), [2046, 2047, 2048, 2049]]))
+    cols = np.unique(np.concatenate([_sample(O, 300, 6), np.arange(O - 40, O), np.arange(21760, 21790)]))
+    _sampled_linear_check(sq, bf16_round(x), None, 2, 4, bf16_round(w), rows, cols)

@@ -23,6 +23,8 @@ __all__ = [
     "quantize_mxfp4",
     "linear",
     "linear_grouped",
+    "linear_silu_prepare",
+    "linear_silu_prepare_into",
     "silu_mul",
     "SharqError",
     "status_string",
@@ -201,6 +203,55 @@ def linear_grouped(prep: Prepared, w: MXFP4, seg_offsets, a_rows=None, out=None)
                    _stream(out.device))
     _lib.check("sharq_linear_grouped", st)
     return out
+
+
+def linear_silu_prepare(prep: Prepared, w_gu: MXFP4, n: int = 2, m: int = 4, with_h: bool = False,
+                        with_prepared: bool = True, with_mask: bool = True):
+    """Fused gate|up projection: Y = two-path GEMM of prep against w_gu (rows:
+    I gate rows, then I up rows), h = bf16(silu(Y[:, :I]) * Y[:, I:]), then
+    prepare(h, n, m). Returns (Prepared of h or None, h or None); the results
+    equal linear -> silu_mul -> prepare bit for bit."""
+    torch = _torch()
+    _check_prepared(prep)
+    _need(w_gu.codes, torch.uint8, "w_gu.codes", 3)
+    _need(w_gu.scales, torch.uint8, "w_gu.scales", 3)
+    T, K = prep.bb_codes.shape[1], prep.K
+    O = w_gu.codes.shape[1]
+    if w_gu.K != K or O % 2:
+        raise ValueError("w_gu must be [2I, K] with the activation's K")
+    _check_stage_major(w_gu.codes, w_gu.scales, O, K, "w_gu")
+    I = O // 2
+    dev = prep.bb_codes.device
+    kw = dict(dtype=torch.uint8, device=dev)
+    h = torch.empty((T, I), dtype=torch.bfloat16, device=dev) if with_h else None
+    hp = None
+    if with_prepared:
+        G = stages(I)
+        hp = Prepared(torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
+                      torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
+                      torch.empty((T, I // 8), **kw) if with_mask else None, I)
+    _fused_call(prep, w_gu, T, I, K, n, m, h, hp)
+    return hp, h
+
+
+def linear_silu_prepare_into(prep: Prepared, w_gu: MXFP4, out: Prepared, n: int = 2, m: int = 4) -> Prepared:
+    """linear_silu_prepare writing prepare(h) into preallocated `out` (no h)."""
+    _check_prepared(prep)
+    _check_prepared(out)
+    T, K, I = prep.bb_codes.shape[1], prep.K, out.K
+    if w_gu.K != K or tuple(w_gu.codes.shape) != (stages(K), 2 * I, 64) or out.bb_codes.shape[1] != T:
+        raise ValueError("shapes of prep, w_gu and out do not match")
+    _fused_call(prep, w_gu, T, I, K, n, m, None, out)
+    return out
+
+
+def _fused_call(prep, w_gu, T, I, K, n, m, h, hp):
+    st = _lib.call("sharq_linear_silu_prepare", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
+                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), w_gu.codes.data_ptr(),
+                   w_gu.scales.data_ptr(), T, I, K, n, m, _ptr(h),
+                   _ptr(hp and hp.bb_codes), _ptr(hp and hp.bb_scales), _ptr(hp and hp.res_codes),
+                   _ptr(hp and hp.res_scales), _ptr(hp and hp.mask), _stream(prep.bb_codes.device))
+    _lib.check("sharq_linear_silu_prepare", st)
 
 
 def silu_mul(gu, out=None):

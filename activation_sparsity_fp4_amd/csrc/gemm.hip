@@ -45,8 +45,10 @@
 // accumulator's register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l % 32.
 
+#include "prepare_block.h"
 #include "sharq_device.h"
 #include "sharq_internal.h"
+#include "silu.h"
 
 namespace sharq {
 namespace {
@@ -123,6 +125,22 @@ struct TileRows {
     if (r >= rows_valid) return -1;
     const int64_t p = m0 + r;
     return gather ? (int64_t)gather[p] : p;
+  }
+};
+
+// Weight rows of one output tile: the weight row behind tile column c.
+// Plain tiles take rows n0 + c. A fused gate|up tile over h columns
+// [h0, h0 + 128) of a weight whose rows are [gate (I rows); up (I rows)]
+// alternates 64-row blocks: block b = c / 64 holds the gate (b even) or up
+// (b odd) rows of h columns h0 + 64 (b / 2) + c % 64, so each wave's four
+// 32-column MFMA tiles are gate, gate, up, up of the same 64 h columns.
+struct TileCols {
+  int64_t n0;    // first output column (plain) or first h column (gate|up)
+  int64_t half;  // 0 for a plain tile, else I
+  __device__ __forceinline__ int64_t w_row(int c) const {
+    if (half == 0) return n0 + c;
+    const int b = c >> 6;
+    return ((b & 1) ? half : 0) + n0 + 64 * (b >> 1) + (c & 63);
   }
 };
 
@@ -311,7 +329,7 @@ __device__ __forceinline__ void ring_iter(const RingLoader<C>& ld, uint8_t* cur,
 // by the ring length makes the register allocator rotate fragment registers
 // between copies and, at 256 accumulators, spill.
 template <class C>
-__device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows& tr, int64_t n0, uint8_t* ring,
+__device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows& tr, const TileCols& tc, uint8_t* ring,
                                               v16f (&acc)[C::WM][C::WN]) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -343,7 +361,7 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   for (int j = 0; j < C::kWChunks; ++j) {
     const int row = 16 * (wave + 4 * j) + (lane >> 2);
     const int part = (lane & 3) ^ swz_part(row);
-    const int64_t o = n0 + row;
+    const int64_t o = tc.w_row(row);
     ld.w_off[j] = o < op.O ? (uint32_t)(o * kRowBytes + part * 16) : kOOB;
   }
   // scale runs: 64-row run q of [backbone rows | residual rows | weight rows]
@@ -357,7 +375,7 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
       ld.s_off[i] = src >= 0 ? (uint32_t)(src * 4) : kOOB;
       ld.s_is_w[i] = false;
     } else {
-      const int64_t o = n0 + 64 * (q - 2 * qa) + lane;
+      const int64_t o = tc.w_row(64 * (q - 2 * qa) + lane);
       ld.s_rsrc[i] = ws_rsrc;
       ld.s_off[i] = o < op.O ? (uint32_t)(o * 4) : kOOB;
       ld.s_is_w[i] = true;
@@ -564,7 +582,7 @@ __global__ __launch_bounds__(kThreads, kRingPath ? C::kOccupancy : 1) void linea
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring<C>(op, tr, n0, lds, acc);
+    mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc);
   else
     mainloop_regs(op, tr, n0, lds, lds + C::kStage, acc);
   store_tile<C>(acc, y, ldy, tr.m0, tr.rows_valid, n0, op.O);
@@ -624,10 +642,116 @@ __global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) vo
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring<C>(op, tr, n0, lds, acc);
+    mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc);
   else
     mainloop_regs(op, tr, n0, lds, lds + C::kStage, acc);
   store_tile<C>(acc, y, op.O, tr.m0, tr.rows_valid, n0, op.O);
+}
+
+// ---------------------------------------------------------------------------
+// Fused gate|up projection: two-path GEMM -> silu(gate) * up -> prepare.
+// ---------------------------------------------------------------------------
+
+// Outputs of the fused epilogue: h itself and/or its prepared form (the
+// activation of the down projection), each optional.
+struct HOutputs {
+  uint16_t* h;  // bf16 [T][I] or nullptr
+  uint8_t* bb_codes;  // [I/128][T][64] or nullptr (then no prepared output)
+  uint8_t* bb_scales;
+  uint8_t* res_codes;
+  uint8_t* res_scales;
+  uint8_t* mask;  // [T][I/8] or nullptr
+  int64_t T, I;
+};
+
+constexpr int kHStride = 272;  // bytes per h row in LDS: 256 + 16 keeps row starts on distinct banks
+
+// The tile's h = bf16(silu(gate) * up) (128 rows x 128 h columns) goes
+// through LDS so that each lane then owns whole 32-entry blocks of h rows:
+// 512 (row, block) pairs, two per lane, each coded by the same per-block
+// prepare arithmetic as the prepare kernel.
+template <int N, int M>
+__device__ __forceinline__ void silu_prepare_epilogue(const v16f (&acc)[2][4], uint8_t* lds, const TileRows& tr,
+                                                      int64_t h0, const HOutputs& out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  ring_barrier();  // every wave is done with the ring before it is overwritten
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = 64 * wn + 32 * j + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const uint32_t hb = bf16_rne_bits(silu_times(acc[i][j][r], acc[i][j + 2][r]));
+        *reinterpret_cast<uint16_t*>(lds + row * kHStride + 2 * col) = (uint16_t)hb;
+      }
+    }
+  __syncthreads();
+  const int64_t blk0 = h0 >> 5;  // first 32-block of the tile along I
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int p = tid + 256 * k;
+    const int row = p >> 2, blk = p & 3;
+    if (row >= tr.rows_valid) continue;
+    const int64_t t = tr.m0 + row;
+    const uint4* src = reinterpret_cast<const uint4*>(lds + row * kHStride + 64 * blk);
+    uint4 raw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) raw[q] = src[q];
+    if (out.h) {
+      uint4* dst = reinterpret_cast<uint4*>(out.h + t * out.I + h0 + 32 * blk);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = raw[q];
+    }
+    if (out.bb_codes) {
+      float xv[32];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[8 * q + 2 * e] = bf16_lo(w[e]);
+          xv[8 * q + 2 * e + 1] = bf16_hi(w[e]);
+        }
+      }
+      const PreparedBlock pb = prepare_block<N, M, false>(xv);
+      const uint32_t b = (uint32_t)(blk0 + blk);
+      *reinterpret_cast<uint4*>(out.bb_codes + code_offset(t, b, out.T)) = pb.c_bb;
+      *reinterpret_cast<uint4*>(out.res_codes + code_offset(t, b, out.T)) = pb.c_rs;
+      out.bb_scales[scale_index(t, b, out.T)] = (uint8_t)pb.e_bb;
+      out.res_scales[scale_index(t, b, out.T)] = (uint8_t)pb.e_rs;
+      if (out.mask) reinterpret_cast<uint32_t*>(out.mask)[t * (out.I >> 5) + b] = pb.keep;
+    }
+  }
+}
+
+// One 128 x 128 h tile: the two-path GEMM over the tile's 128 gate and 128 up
+// weight rows, then the fused epilogue.
+template <class C, int N, int M>
+__global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_kernel(Operands op, HOutputs out,
+                                                                                      int tiles_m, int tiles_total) {
+  static_assert(C::WM == 2 && C::WN == 4, "the epilogue assumes 128 x 256 tiles");
+  static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
+  SHARQ_GEMM_LDS(C, true)
+  int tile = blockIdx.x;
+  if ((tiles_total & 7) == 0) {
+    const int per_xcd = tiles_total >> 3;
+    tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  }
+  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  TileRows tr;
+  tr.m0 = (int64_t)tm * C::BM;
+  tr.rows_valid = out.T - tr.m0 < C::BM ? out.T - tr.m0 : C::BM;
+  tr.gather = nullptr;
+  const int64_t h0 = (int64_t)tn * 128;
+  v16f acc[C::WM][C::WN];
+  zero_acc<C>(acc);
+  mainloop_ring<C>(op, tr, TileCols{h0, out.I}, lds, acc);
+  silu_prepare_epilogue<N, M>(acc, lds, tr, h0, out);
 }
 
 Operands make_operands(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
@@ -698,6 +822,28 @@ hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scal
   else
     hipLaunchKernelGGL(linear_grouped_kernel<false>, grid, dim3(kThreads), 0, stream, op, a_rows, seg_offsets, E,
                        w_codes, w_scales, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                                      const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                                      int64_t T, int64_t I, int64_t K, int n, int m, uint16_t* h,
+                                      uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
+                                      uint8_t* h_res_scales, uint8_t* h_mask, hipStream_t stream) {
+  const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, 2 * I, K);
+  const HOutputs out{h, h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, T, I};
+  const int tiles_m = (int)((T + 127) / 128);
+  const int total = tiles_m * (int)(I / 128);
+  const bool two = total >= kTwoPerCu;
+#define SHARQ_FUSED(C, NN, MM)                                                                                    \
+  hipLaunchKernelGGL((linear_silu_prepare_kernel<C, NN, MM>), dim3(total), dim3(kThreads), 0, stream, op, out, \
+                     tiles_m, total)
+  if (n == 2 && m == 4) {
+    if (two) SHARQ_FUSED(SmallTile, 2, 4); else SHARQ_FUSED(DeepTile, 2, 4);
+  } else {
+    if (two) SHARQ_FUSED(SmallTile, 8, 16); else SHARQ_FUSED(DeepTile, 8, 16);
+  }
+#undef SHARQ_FUSED
   return hipGetLastError();
 }
 

@@ -4,28 +4,11 @@
 // HBM-bound elementwise kernel: each lane reads 8 gate and 8 up floats
 // (2 x 32 B) and writes 8 bf16 (16 B).
 
-#include "sharq_device.h"
 #include "sharq_internal.h"
+#include "silu.h"
 
 namespace sharq {
 namespace {
-
-__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  const uint32_t b = __float_as_uint(f);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
-// silu(g) * u without overflow: with h = exp(-|g| / 2) (in (0, 1]),
-//   g >= 0: g * u / (1 + h^2)           (h^2 = exp(-g))
-//   g <  0: ((g * u) * h) * h / (1 + h^2)  (= g u e^g / (1 + e^g))
-// The negative branch multiplies by the two half-exponentials one at a time so
-// results down to the fp32 normal range survive even when e^g alone is subnormal.
-__device__ __forceinline__ float silu_times(float g, float u) {
-  const float h = __expf(-0.5f * fabsf(g));
-  const float den = 1.0f + h * h;
-  const float gu = g * u;
-  return g >= 0.0f ? gu / den : ((gu * h) * h) / den;
-}
 
 __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ gu, int64_t I, uint32_t groups_per_row,
                                                        uint32_t total, uint16_t* __restrict__ h) {

@@ -55,6 +55,12 @@ def silu_bytes(T, I):
     return T * (8 * I + 2 * I)
 
 
+def fused_bytes(T, I, H):
+    """Minimum HBM bytes of the fused gate|up stage: both A operands, the [2I x H]
+    weight, and prepare(h) written (codes, scales, mask)."""
+    return 2 * T * H * 17 / 32 + 2 * I * H * 17 / 32 + T * I * (0.5 + 0.5 + 2 / 32 + 1 / 8)
+
+
 def _to_gpu_bf16(torch, u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -65,7 +71,7 @@ class Stage:
         self.bytes, self.flops_alg, self.flops_exec = bytes_, flops_alg, flops_exec
 
 
-def build_workload(name, torch, sq):
+def build_workload(name, torch, sq, unfused=False):
     """Returns (stages, tokens_per_step, config dict, oracle sample fn)."""
     from synth import (workload_down_silu, workload_linear, workload_llama70b_decode, workload_llama8b_mlp,
                        workload_qwen3_moe)
@@ -77,22 +83,34 @@ def build_workload(name, torch, sq):
         w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"]))
         buf = {}
         buf["p1"] = sq.prepare(x, g, 2, 4)
-        buf["gu"] = sq.linear(buf["p1"], w_gu)
-        buf["h"] = sq.silu_mul(buf["gu"])
-        buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
-        buf["y"] = sq.linear(buf["p2"], w_dn)
         fa1, fe1 = gemm_flops(T, 2 * I, H)
         fa2, fe2 = gemm_flops(T, H, I)
-        stages = [
-            Stage("prepare_x_gamma", lambda: sq.prepare(x, g, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(T, H, True)),
-            Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "mfma", gemm_bytes(T, 2 * I, H),
-                  fa1, fe1),
-            Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
-            Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm", prepare_bytes(T, I)),
+        if unfused:
+            buf["gu"] = sq.linear(buf["p1"], w_gu)
+            buf["h"] = sq.silu_mul(buf["gu"])
+            buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
+            middle = [
+                Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "mfma",
+                      gemm_bytes(T, 2 * I, H), fa1, fe1),
+                Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
+                Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
+                      prepare_bytes(T, I)),
+            ]
+        else:
+            buf["p2"], _ = sq.linear_silu_prepare(buf["p1"], w_gu, 2, 4)
+            middle = [
+                Stage("gemm_gate_up_silu_prepare",
+                      lambda: sq.linear_silu_prepare_into(buf["p1"], w_gu, buf["p2"], 2, 4), "mfma",
+                      fused_bytes(T, I, H), fa1, fe1),
+            ]
+        buf["y"] = sq.linear(buf["p2"], w_dn)
+        stages = [Stage("prepare_x_gamma", lambda: sq.prepare(x, g, 2, 4, out=buf["p1"]), "hbm",
+                        prepare_bytes(T, H, True))] + middle + [
             Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "mfma", gemm_bytes(T, H, I), fa2, fe2),
         ]
         cfg = {"workload": "Llama-3.1-8B MLP block, 2048-token prefill, 2:4, MXFP4, RMSNorm gamma absorbed",
-               "tokens": T, "hidden": H, "intermediate": I, "nm": "2:4", "seed": 1002}
+               "tokens": T, "hidden": H, "intermediate": I, "nm": "2:4", "seed": 1002,
+               "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)"}
 
         def oracle_sample(rows):
             from oracle import linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref
@@ -264,6 +282,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_mlp", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="llama8b_mlp: run gate|up, silu_mul and prepare(h) as three kernels")
     ap.add_argument("--profile-stage", default=None,
                     help="run only this stage in warmup and timing (per-kernel profiling; not a step)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -283,7 +303,7 @@ def main():
         copy_calibration(args.copy_bytes, args.steps)
         return
     print(f"# building inputs for {args.workload}", file=sys.stderr, flush=True)
-    stages, tokens, cfg, oracle_sample = build_workload(args.workload, torch, sq)
+    stages, tokens, cfg, oracle_sample = build_workload(args.workload, torch, sq, args.unfused)
     torch.cuda.synchronize()
     if args.profile_stage:
         stages = [s for s in stages if s.name == args.profile_stage]

@@ -150,6 +150,34 @@ SHARQ_API int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_sc
                          hipStream_t stream);
 
 /*
+ * sharq_linear_silu_prepare -- a fused gate|up projection of a gated MLP:
+ * the two-path FP4 GEMM of sharq_linear against a weight whose 2I rows are
+ * the gate rows (0 .. I-1) followed by the up rows (I .. 2I-1), then
+ *   h[t][i] = bf16(silu(Y[t][i]) * Y[t][I + i])      (as sharq_silu_mul)
+ * and then the prepare operator on h (as sharq_prepare with no gamma), so
+ * that h never round-trips through HBM in fp32 (glue around the method; the
+ * two-path GEMM and the prepare are the SharQ page's, Abstract and
+ * Section 1).
+ *  bb_codes/res_codes u8 [G][T][64], bb_scales/res_scales u8 [G][T][4]: the
+ *              prepared input rows (G = K / 128);
+ *  w_codes u8 [G][2I][64], w_scales u8 [G][2I][4]: the fused weight;
+ *  h           bf16 [T][I] or NULL;
+ *  h_bb_codes, h_res_codes u8 [I/128][T][64], h_bb_scales, h_res_scales
+ *              u8 [I/128][T][4], h_mask u8 [T][I/8] (or NULL): prepare(h)
+ *              with pattern n:m, or all four NULL (then h must be given).
+ * Outputs are bit-identical to sharq_linear + sharq_silu_mul + sharq_prepare
+ * run one after the other. Requires I % 128 == 0 and K % 128 == 0
+ * (SHARQ_ENOTIMPL otherwise), T * K / 2 < 2^31 and I * K < 2^31.
+ */
+SHARQ_API int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                              const uint8_t* res_codes, const uint8_t* res_scales,
+                              const uint8_t* w_codes, const uint8_t* w_scales,
+                              int64_t T, int64_t I, int64_t K, int n, int m,
+                              uint16_t* h, uint8_t* h_bb_codes, uint8_t* h_bb_scales,
+                              uint8_t* h_res_codes, uint8_t* h_res_scales, uint8_t* h_mask,
+                              hipStream_t stream);
+
+/*
  * sharq_silu_mul -- glue between a fused gate|up projection and the down
  * projection (not part of the method): h[t][i] = bf16(silu(g) * u) with
  * g = gu[t][i], u = gu[t][I + i], silu(g) = g / (1 + exp(-g)), fp32 math,

@@ -127,3 +127,30 @@ def test_python_wrappers_refuse_cpu_tensors():
         sq.prepare(torch.zeros((2, 64), dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         sq.silu_mul(torch.zeros((2, 16), dtype=torch.float32))
+
+
+def fused(T=4, I=128, K=128, n=2, m=4, h=G, hbc=A + 0x100000, hbs=B + 0x100000, hrc=C + 0x100000,
+          hrs=D + 0x100000, hmask=0, **kw):
+    args = dict(bc=A, bs=B, rc=C, rs=D, wc=E_, ws=F)
+    args.update(kw)
+    return _lib.call("sharq_linear_silu_prepare", args["bc"], args["bs"], args["rc"], args["rs"], args["wc"],
+                     args["ws"], T, I, K, n, m, h, hbc, hbs, hrc, hrs, hmask, 0)
+
+
+def test_linear_silu_prepare_validation():
+    assert fused(T=0) == _lib.SHARQ_OK
+    assert fused(T=0, h=0) == _lib.SHARQ_OK                   # prepared output only
+    assert fused(T=0, hbc=0, hbs=0, hrc=0, hrs=0) == _lib.SHARQ_OK  # h only
+    assert fused(hbc=0, hbs=0, hrc=0, hrs=0, h=0) == _lib.SHARQ_EINVAL  # nothing to write
+    assert fused(hbs=0) == _lib.SHARQ_EINVAL                  # prepared output half given
+    assert fused(hbc=0, hbs=0, hrc=0, hrs=0, hmask=A) == _lib.SHARQ_EINVAL  # mask without prepare
+    assert fused(n=4, m=8) == _lib.SHARQ_EUNSUPPORTED
+    assert fused(T=-1) == _lib.SHARQ_EINVAL
+    assert fused(K=96) == _lib.SHARQ_ENOTIMPL                  # K % 128
+    assert fused(I=96) == _lib.SHARQ_ENOTIMPL                  # I % 128
+    assert fused(I=100) == _lib.SHARQ_EINVAL                   # I % 32
+    assert fused(bc=0) == _lib.SHARQ_EINVAL
+    assert fused(wc=E_ + 4) == _lib.SHARQ_EALIGN
+    assert fused(h=G + 2) == _lib.SHARQ_EALIGN
+    assert fused(hmask=F + 8) == _lib.SHARQ_EALIGN
+    assert fused(T=1 << 20, K=1 << 12) == _lib.SHARQ_ENOTIMPL  # activation codes past 32-bit offsets

@@ -1,0 +1,88 @@
+"""GPU parity of the fused gate|up entry point (two-path GEMM -> silu(gate) * up
+-> prepare) against the unfused chain linear -> silu_mul -> prepare, which the
+other GPU tests check against the oracle.
+
+The fused kernel runs the same MFMA sequence per output element as the plain
+GEMM and the same SiLU and per-block prepare code, so h, codes, scales and
+masks must match the unfused chain bit for bit. On sampled rows the fused
+outputs are also checked against the oracle directly: prepare_ref of the
+fused h must reproduce the fused codes, scales and mask, and h must be the
+correctly rounded silu(g) * u of the GPU's GEMM output to one bf16 ulp.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import prepare_ref, silu_mul_ref
+from synth import bf16_round, workload_llama8b_mlp
+from gpu_util import assert_bf16_close, assert_prepare_equal, bf16_to_gpu, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import activation_sparsity_fp4_amd as sq
+    return sq
+
+
+FIELDS = ("bb_codes", "bb_scales", "res_codes", "res_scales", "mask")
+
+
+def _inputs(T, I, K, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((T, K)) * rng.lognormal(0, 0.5, (T, 1))).astype(np.float32)
+    x[:, rng.choice(K, max(1, K // 200), replace=False)] *= 50
+    w = (rng.standard_normal((2 * I, K)) * 0.02).astype(np.float32)
+    return bf16_round(x), bf16_round(w)
+
+
+def _check_fused(sq, x_bits, gamma_bits, w_bits, n, m, rows_sample):
+    import torch
+    T, K = x_bits.shape
+    I = w_bits.shape[0] // 2
+    p1 = sq.prepare(bf16_to_gpu(x_bits), None if gamma_bits is None else bf16_to_gpu(gamma_bits), 2, 4)
+    w = sq.quantize_mxfp4(bf16_to_gpu(w_bits))
+    # unfused chain
+    y = sq.linear(p1, w)
+    h_ref = sq.silu_mul(y)
+    p2_ref = sq.prepare(h_ref, None, n, m)
+    # fused, all outputs
+    hp, h = sq.linear_silu_prepare(p1, w, n, m, with_h=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(h), to_np(h_ref)), "fused h differs from linear -> silu_mul"
+    for f in FIELDS:
+        assert np.array_equal(to_np(getattr(hp, f)), to_np(getattr(p2_ref, f))), f"fused {f} differs"
+    # prepared output only, without the mask; h only
+    hp2, h2 = sq.linear_silu_prepare(p1, w, n, m, with_h=False, with_mask=False)
+    assert h2 is None and hp2.mask is None
+    for f in FIELDS[:4]:
+        assert np.array_equal(to_np(getattr(hp2, f)), to_np(getattr(p2_ref, f)))
+    hp3, h3 = sq.linear_silu_prepare(p1, w, n, m, with_h=True, with_prepared=False)
+    assert hp3 is None and np.array_equal(to_np(h3), to_np(h_ref))
+    # oracle on sampled rows
+    h_np = to_np(h)
+    rows = rows_sample
+    assert_prepare_equal(hp, prepare_ref(h_np[rows], None, n, m), rows=rows)
+    assert_bf16_close(h_np[rows], silu_mul_ref(to_np(y)[rows], I))
+
+
+@pytest.mark.parametrize("T,I,K,n,m", [(300, 256, 512, 2, 4), (1, 128, 128, 2, 4), (130, 384, 1024, 8, 16),
+                                       (2048, 4096, 512, 2, 4), (129, 128, 256, 8, 16)])
+def test_fused_matches_unfused(sq, T, I, K, n, m):
+    # (2048, 4096): 512 tiles, the two-workgroups-per-CU kernel; the others the 4-stage ring
+    print(f"fused gate|up T={T} I={I} K={K} {n}:{m}", flush=True)
+    x, w = _inputs(T, I, K, seed=T + I + K)
+    rows = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(1).choice(T, min(T, 24), replace=False)]))
+    _check_fused(sq, x, None, w, n, m, rows)
+
+
+def test_fused_llama8b_gate_up_full_size(sq):
+    # the benchmark's fused stage: 2048 x 4096 -> gate|up 2 x 14336, gamma absorbed in the first prepare
+    print("fused gate|up workload llama8b 2048x4096 -> 2x14336", flush=True)
+    wl = workload_llama8b_mlp()
+    rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(2).choice(2048, 24, replace=False)]))
+    _check_fused(sq, wl["x"], wl["gamma"], wl["w_gu"], 2, 4, rows)

@@ -71,16 +71,19 @@ struct Tile {
   static constexpr int kOffSAs = kOffW + BN * kRowBytes;
   static constexpr int kOffSAr = kOffSAs + BM * 4;
   static constexpr int kOffSW = kOffSAr + BM * 4;
-  static constexpr int kStage = kOffSW + BN * 4;
-  static constexpr int kRing = RING_;
-  static constexpr int kOccupancy = kLdsBytes / (kRing * kStage);  // workgroups per CU (LDS bound)
   // buffer->LDS instructions per wave per stage: 1 KB code chunks of each
-  // activation operand, of the weight, and 256-byte scale runs (64 rows)
+  // activation operand, of the weight, and 256-byte scale runs (64 rows).
+  // When the scale runs do not split evenly over the four waves, the spare
+  // instructions read nothing (out of range) into a trash area, so that every
+  // wave issues the same number of loads per stage.
   static constexpr int kAChunks = BM / 64;
   static constexpr int kWChunks = BN / 64;
-  static constexpr int kSLoads = (2 * BM + BN) / 256;
+  static constexpr int kSRuns = (2 * BM + BN) / 64;
+  static constexpr int kSLoads = (kSRuns + 3) / 4;
   static constexpr int kLoads = 2 * kAChunks + kWChunks + kSLoads;
-  static_assert((2 * BM + BN) % 256 == 0, "scale runs must split evenly over the four waves");
+  static constexpr int kStage = kOffSW + BN * 4 + 256 * (4 * kSLoads - kSRuns);
+  static constexpr int kRing = RING_;
+  static constexpr int kOccupancy = kLdsBytes / (kRing * kStage);  // workgroups per CU (LDS bound)
   static_assert(kRing >= 2 && kRing * kStage <= kLdsBytes, "ring");
 };
 using SmallTile = Tile<2, 4, 2>;  // 128 x 256, 34 KB stages, ring of 2, two workgroups per CU
@@ -305,22 +308,28 @@ __device__ __forceinline__ void ring_iter(const RingLoader<C>& ld, uint8_t* cur,
   constexpr int kReads = 2 * C::WM + C::WN;   // fragment reads of a sub-step
   constexpr int kMfma = 2 * C::WM * C::WN;    // MFMAs of a sub-step
   read_frags<C, 1>(cur, f1, wm, wn, lr, lh);
+  // a wave issuing its MFMA group gets issue priority over a wave of the
+  // other workgroup on the SIMD that is loading or waiting
+  __builtin_amdgcn_s_setprio(1);
   mfma_sub<C, 0>(f0, c, acc);
   // schedule: the fragment reads first, then the MFMAs
   __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   wait_vmcnt<(C::kRing - 2) * C::kLoads>();  // batch s+1 landed; later batches may be in flight
   ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
   ld.issue(cur, s + C::kRing);
   read_scales<C>(next, cn, wm, wn, lr, lh);
   read_frags<C, 0>(next, f0, wm, wn, lr, lh);
+  __builtin_amdgcn_s_setprio(1);
   mfma_sub<C, 1>(f1, c, acc);
   // schedule: all LDS reads of stage s+1 first, then the MFMAs
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * kReads, 0);
   __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
   __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   c = cn;
 }
 
@@ -369,7 +378,11 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   for (int i = 0; i < C::kSLoads; ++i) {
     const int q = wave + 4 * i;
     constexpr int qa = C::BM / 64;
-    if (q < 2 * qa) {
+    if (q >= C::kSRuns) {  // spare instruction: reads nothing, lands in the trash area
+      ld.s_rsrc[i] = ws_rsrc;
+      ld.s_off[i] = kOOB;
+      ld.s_is_w[i] = true;
+    } else if (q < 2 * qa) {
       const int64_t src = tr.src(64 * (q % qa) + lane);
       ld.s_rsrc[i] = q < qa ? as_rsrc0 : as_rsrc1;
       ld.s_off[i] = src >= 0 ? (uint32_t)(src * 4) : kOOB;
@@ -557,23 +570,41 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[C::WM][C::WN], floa
     }
 }
 
+// Tile order. Workgroups are dispatched round-robin over the 8 XCDs, each
+// with its own L2; block b is remapped so that each XCD receives a contiguous
+// range of tile indices. Inside a range, tiles go in groups of 4 row tiles:
+// the group's column tiles are walked with the 4 row tiles innermost, so the
+// tiles in flight on one XCD share 4 activation row tiles and a few weight
+// column tiles (measured 2-6% faster than row tiles innermost over all rows).
+struct TileIndex {
+  int tm, tn;
+};
+__device__ __forceinline__ TileIndex tile_index(int b, int tiles_m, int tiles_total) {
+  int tile = b;
+  if ((tiles_total & 7) == 0) {
+    const int per_xcd = tiles_total >> 3;
+    tile = (b & 7) * per_xcd + (b >> 3);
+  }
+  constexpr int kGroup = 4;
+  const int tiles_n = tiles_total / tiles_m;
+  const int group = tile / (kGroup * tiles_n);
+  const int first_m = group * kGroup;
+  const int gsize = min(tiles_m - first_m, kGroup);
+  const int in_group = tile - group * kGroup * tiles_n;
+  return TileIndex{first_m + in_group % gsize, in_group / gsize};
+}
+
 // LDS of the main loops: the ring's stages, or the general path's double buffer.
 #define SHARQ_GEMM_LDS(C, kRingPath) \
   __shared__ __attribute__((aligned(16))) uint8_t lds[(kRingPath ? C::kRing : 2) * C::kStage];
 
-// Plain two-path GEMM. Tiles are assigned so that each XCD (workgroups are
-// dispatched round-robin over 8 XCDs) receives a contiguous range of tiles;
-// inside a range consecutive tiles share a weight column tile.
+// Plain two-path GEMM, tiles in tile_index order.
 template <class C, bool kRingPath>
 __global__ __launch_bounds__(kThreads, kRingPath ? C::kOccupancy : 1) void linear_kernel(Operands op, int64_t T, float* __restrict__ y,
                                                           int64_t ldy, int tiles_m, int tiles_total) {
   SHARQ_GEMM_LDS(C, kRingPath)
-  int tile = blockIdx.x;
-  if ((tiles_total & 7) == 0) {
-    const int per_xcd = tiles_total >> 3;
-    tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  }
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const TileIndex ti = tile_index(blockIdx.x, tiles_m, tiles_total);
+  const int tm = ti.tm, tn = ti.tn;
   TileRows tr;
   tr.m0 = (int64_t)tm * C::BM;
   tr.rows_valid = T - tr.m0 < C::BM ? T - tr.m0 : C::BM;
@@ -737,12 +768,8 @@ __global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_k
   static_assert(C::WM == 2 && C::WN == 4, "the epilogue assumes 128 x 256 tiles");
   static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
   SHARQ_GEMM_LDS(C, true)
-  int tile = blockIdx.x;
-  if ((tiles_total & 7) == 0) {
-    const int per_xcd = tiles_total >> 3;
-    tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  }
-  const int tm = tile % tiles_m, tn = tile / tiles_m;
+  const TileIndex ti = tile_index(blockIdx.x, tiles_m, tiles_total);
+  const int tm = ti.tm, tn = ti.tn;
   TileRows tr;
   tr.m0 = (int64_t)tm * C::BM;
   tr.rows_valid = out.T - tr.m0 < C::BM ? out.T - tr.m0 : C::BM;

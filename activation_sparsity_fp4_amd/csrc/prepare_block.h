@@ -24,8 +24,11 @@ namespace sharq {
 
 // Mask bits (one per entry, bit k) of the kept entries of a block for n:m.
 template <int N, int M>
-__device__ __forceinline__ uint32_t select_fast(const float (&x)[32]) {
+__device__ __forceinline__ uint32_t select_fast(const float (&x)[32], float (&xs)[32]) {
   static_assert((N == 2 && M == 4) || (N == 8 && M == 16), "pattern");
+  // Entry k is kept when its key is at least the group's N-th largest key;
+  // one compare per entry yields both its mask bit and its backbone value
+  // (xs[k] = x[k] when kept, 0 otherwise).
   uint32_t mask = 0;
   if constexpr (M == 4) {
 #pragma unroll
@@ -38,7 +41,11 @@ __device__ __forceinline__ uint32_t select_fast(const float (&x)[32]) {
       const uint32_t c = max(k[2], k[3]), d = min(k[2], k[3]);
       const uint32_t second = max(max(min(a, c), b), d);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mask |= (k[i] >= second ? 1u : 0u) << (4 * g + i);
+      for (int i = 0; i < 4; ++i) {
+        const bool kept = k[i] >= second;
+        xs[4 * g + i] = kept ? x[4 * g + i] : 0.0f;
+        mask |= kept ? 1u << (4 * g + i) : 0u;
+      }
     }
   } else {
 #pragma unroll
@@ -62,7 +69,11 @@ __device__ __forceinline__ uint32_t select_fast(const float (&x)[32]) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) thr = min(thr, max(lo[i], hi[7 - i]));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mask |= (k[i] >= thr ? 1u : 0u) << (16 * g + i);
+      for (int i = 0; i < 16; ++i) {
+        const bool kept = k[i] >= thr;
+        xs[16 * g + i] = kept ? x[16 * g + i] : 0.0f;
+        mask |= kept ? 1u << (16 * g + i) : 0u;
+      }
     }
   }
   return mask;
@@ -102,27 +113,28 @@ struct PreparedBlock {
 template <int N, int M, bool kMaybeLowBits>
 __device__ __forceinline__ PreparedBlock prepare_block(const float (&xv)[32]) {
   PreparedBlock out;
-  // N:M selection
+  // N:M selection; xs = the backbone (kept entries, zeros elsewhere)
   uint32_t keep;
+  float xs[32];
   if constexpr (kMaybeLowBits) {
     uint32_t low = 0;
 #pragma unroll
     for (int k = 0; k < 32; ++k) low |= __float_as_uint(xv[k]);
-    if (low & (uint32_t)(M - 1))
+    if (low & (uint32_t)(M - 1)) {
       keep = select_exact<N, M>(xv);
-    else
-      keep = select_fast<N, M>(xv);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) xs[k] = (keep >> k) & 1u ? xv[k] : 0.0f;
+    } else {
+      keep = select_fast<N, M>(xv, xs);
+    }
   } else {
-    keep = select_fast<N, M>(xv);
+    keep = select_fast<N, M>(xv, xs);
   }
 
   // backbone: the block's largest |x'| is always kept (each group keeps its
   // maximum), so the backbone scale is the block's plain MX scale
   const uint32_t e_bb = e8m0_from_amax_bits(amax_bits32(xv));
   const float s_bb = scale_from_e8m0(e_bb);
-  float xs[32];
-#pragma unroll
-  for (int k = 0; k < 32; ++k) xs[k] = (keep >> k) & 1u ? xv[k] : 0.0f;
   const uint4 c_bb = quantize32(xs, s_bb);
 
   // residual against the quantised backbone (exact in fp32)

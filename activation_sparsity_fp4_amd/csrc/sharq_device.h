@@ -81,13 +81,16 @@ __device__ __forceinline__ int64_t code_offset(int64_t row, uint32_t block, int6
   return (int64_t)(block >> 2) * rows * 64 + row * 64 + (block & 3) * 16;
 }
 
-// Largest |v| of 32 floats as a bit pattern (sign cleared). Integer max on
-// the magnitude bits orders non-negative floats exactly.
+// Largest |v| of 32 finite floats as a bit pattern (sign cleared). A float
+// max of magnitudes (abs is a free input modifier, three inputs per
+// instruction) returns exactly the largest magnitude; if denormals were
+// flushed only blocks whose largest magnitude is subnormal could differ, and
+// those get scale byte 0 either way.
 __device__ __forceinline__ uint32_t amax_bits32(const float (&v)[32]) {
-  uint32_t m = 0;
+  float m = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) m = max(m, __float_as_uint(v[k]) & 0x7FFFFFFFu);
-  return m;
+  for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(v[k]));
+  return __float_as_uint(m);
 }
 
 }  // namespace sharq

@@ -154,8 +154,25 @@ def quantize_mxfp4(x, out: Optional[MXFP4] = None) -> MXFP4:
     return out
 
 
-def linear(prep: Prepared, w: MXFP4, out=None):
-    """Two-path FP4 GEMM: Y = deq(backbone) W^T + deq(residual) W^T, fp32 [T, O]."""
+_workspaces = {}
+
+
+def _workspace(device, nbytes):
+    """A device workspace of at least nbytes for split-K calls, cached per
+    (device, stream) so that calls on one stream (which never overlap) share it."""
+    torch = _torch()
+    key = (device.index, _stream(device))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def linear(prep: Prepared, w: MXFP4, out=None, split_k: bool = True):
+    """Two-path FP4 GEMM: Y = deq(backbone) W^T + deq(residual) W^T, fp32 [T, O].
+    With split_k, problems with too few output tiles to fill the GPU split K
+    over a cached workspace (sharq_linear_ws); the result is deterministic."""
     torch = _torch()
     _check_prepared(prep)
     _need(w.codes, torch.uint8, "w.codes", 3)
@@ -168,6 +185,14 @@ def linear(prep: Prepared, w: MXFP4, out=None):
     if out is None:
         out = torch.empty((T, O), dtype=torch.float32, device=prep.bb_codes.device)
     _need(out, torch.float32, "out", 2)
+    nbytes = _lib.call("sharq_linear_workspace_bytes", T, O, K) if split_k else 0
+    if nbytes > 0:
+        ws = _workspace(out.device, nbytes)
+        st = _lib.call("sharq_linear_ws", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
+                       prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), w.codes.data_ptr(), w.scales.data_ptr(),
+                       T, O, K, out.data_ptr(), out.stride(0), ws.data_ptr(), ws.numel(), _stream(out.device))
+        _lib.check("sharq_linear_ws", st)
+        return out
     st = _lib.call("sharq_linear", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(), prep.res_codes.data_ptr(),
                    prep.res_scales.data_ptr(), w.codes.data_ptr(), w.scales.data_ptr(), T, O, K,
                    out.data_ptr(), out.stride(0), _stream(out.device))

@@ -30,6 +30,8 @@ SIGNATURES = {
     "sharq_prepare": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _INT, _P, _P, _P, _P, _P, _P]),
     "sharq_quantize_mxfp4": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "sharq_linear": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
+    "sharq_linear_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "sharq_linear_ws": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "sharq_linear_grouped": (_INT, [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _I64, _I64, _I64, _P,
                                     _P]),
     "sharq_linear_silu_prepare": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P,

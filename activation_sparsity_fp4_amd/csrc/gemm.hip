@@ -339,7 +339,7 @@ __device__ __forceinline__ void ring_iter(const RingLoader<C>& ld, uint8_t* cur,
 // between copies and, at 256 accumulators, spill.
 template <class C>
 __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows& tr, const TileCols& tc, uint8_t* ring,
-                                              v16f (&acc)[C::WM][C::WN]) {
+                                              v16f (&acc)[C::WM][C::WN], int s_begin, int s_end) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -395,11 +395,11 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
     }
   }
 
-  const int nsteps = op.nsteps;
-  ld.nsteps = nsteps;
+  // stages [s_begin, s_end) of K (a split-K slice, or all of K)
+  ld.nsteps = s_end;
 #pragma unroll
-  for (int b = 0; b < C::kRing; ++b) ld.issue(ring + b * C::kStage, b);
-  wait_vmcnt<(C::kRing - 1) * C::kLoads>();  // batch 0 landed
+  for (int b = 0; b < C::kRing; ++b) ld.issue(ring + b * C::kStage, s_begin + b);
+  wait_vmcnt<(C::kRing - 1) * C::kLoads>();  // the first batch landed
   ring_barrier();
   Frags<C> f0, f1;
   Scales<C> c, cn;
@@ -407,7 +407,7 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   read_frags<C, 0>(ring, f0, wm, wn, lr, lh);
   int slot = 0;
 #pragma unroll 1
-  for (int s = 0; s < nsteps; ++s) {
+  for (int s = s_begin; s < s_end; ++s) {
     const int nslot = slot + 1 == C::kRing ? 0 : slot + 1;
     ring_iter<C>(ld, ring + slot * C::kStage, ring + nslot * C::kStage, s, f0, f1, c, cn, acc, wm, wn, lr, lh);
     slot = nslot;
@@ -613,10 +613,55 @@ __global__ __launch_bounds__(kThreads, kRingPath ? C::kOccupancy : 1) void linea
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc);
+    mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc, 0, op.nsteps);
   else
     mainloop_regs(op, tr, n0, lds, lds + C::kStage, acc);
   store_tile<C>(acc, y, ldy, tr.m0, tr.rows_valid, n0, op.O);
+}
+
+// Split-K two-path GEMM for problems with few output tiles (decode-sized T,
+// small layers). Workgroup b computes split b % S (stages [S0, S1) of K,
+// S0 = split * nsteps / S) of tile b / S and stores its fp32 partial tile in
+// partials[split] ([S][T][O]); split_reduce_kernel then sums the partials in
+// split order 0, 1, ..., S-1, so the result does not depend on timing. The
+// kernel boundary between the two launches makes the partials visible to
+// every XCD.
+template <class C>
+__global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_split_kernel(Operands op, int64_t T,
+                                                                              int tiles_m, int tiles_total, int S,
+                                                                              float* __restrict__ partials) {
+  SHARQ_GEMM_LDS(C, true)
+  const int split = blockIdx.x % S;
+  const TileIndex ti = tile_index(blockIdx.x / S, tiles_m, tiles_total);
+  TileRows tr;
+  tr.m0 = (int64_t)ti.tm * C::BM;
+  tr.rows_valid = T - tr.m0 < C::BM ? T - tr.m0 : C::BM;
+  tr.gather = nullptr;
+  const int64_t n0 = (int64_t)ti.tn * C::BN;
+  v16f acc[C::WM][C::WN];
+  zero_acc<C>(acc);
+  const int s0 = (int)((int64_t)split * op.nsteps / S), s1 = (int)((int64_t)(split + 1) * op.nsteps / S);
+  mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc, s0, s1);
+  store_tile<C>(acc, partials + (int64_t)split * T * op.O, op.O, tr.m0, tr.rows_valid, n0, op.O);
+}
+
+constexpr int kMaxSplits = 16;
+
+// y[t][o] = sum over q = 0 .. S-1, in that order, of partials[q][t][o]; all
+// S loads of an element are issued before the adds.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partials, int S, int64_t T,
+                                                           int64_t O, float* __restrict__ y, int64_t ldy) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= T * O) return;
+  const int64_t t = e / O, o = e - t * O;
+  float part[kMaxSplits];
+#pragma unroll
+  for (int q = 0; q < kMaxSplits; ++q) part[q] = q < S ? partials[(int64_t)q * T * O + e] : 0.0f;
+  float v = part[0];
+#pragma unroll
+  for (int q = 1; q < kMaxSplits; ++q)
+    if (q < S) v += part[q];
+  y[t * ldy + o] = v;
 }
 
 // Inclusive prefix sum across a 64-lane wave.
@@ -673,7 +718,7 @@ __global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) vo
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc);
+    mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc, 0, op.nsteps);
   else
     mainloop_regs(op, tr, n0, lds, lds + C::kStage, acc);
   store_tile<C>(acc, y, op.O, tr.m0, tr.rows_valid, n0, op.O);
@@ -777,7 +822,7 @@ __global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_k
   const int64_t h0 = (int64_t)tn * 128;
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
-  mainloop_ring<C>(op, tr, TileCols{h0, out.I}, lds, acc);
+  mainloop_ring<C>(op, tr, TileCols{h0, out.I}, lds, acc, 0, op.nsteps);
   silu_prepare_epilogue<N, M>(acc, lds, tr, h0, out);
 }
 
@@ -816,7 +861,60 @@ void launch_tiles(const Operands& op, int64_t T, float* y, int64_t ldy, hipStrea
                      total);
 }
 
+// Split-K plan: problems with at most 256 rows and fewer 128 x 256 tiles
+// than two per CU (and K long enough) split K so that about two workgroups
+// per CU take part, each over at least 4 stages, at most 16 splits, and with
+// the partials' traffic (written and read once: 8 S T O bytes) at most a
+// quarter of the weight's (O K 17/32 bytes), i.e. S <= K / (60 T).
+constexpr int64_t kSplitMaxRows = 256;
+
+struct SplitPlan {
+  int S;             // 1: no split
+  int tiles_m, tiles_total;
+  int64_t partial_bytes;
+};
+
+SplitPlan split_plan(int64_t T, int64_t O, int64_t K) {
+  SplitPlan p{1, 0, 0, 0};
+  if (T <= 0 || T > kSplitMaxRows || O <= 0 || T * O >= ((int64_t)1 << 31) || !ring_path_ok(T, O, K)) return p;
+  p.tiles_m = (int)((T + SmallTile::BM - 1) / SmallTile::BM);
+  p.tiles_total = p.tiles_m * (int)((O + SmallTile::BN - 1) / SmallTile::BN);
+  const int64_t nsteps = K / 128;
+  int64_t S = kTwoPerCu / p.tiles_total;
+  S = S < nsteps / 4 ? S : nsteps / 4;
+  S = S < kMaxSplits ? S : kMaxSplits;
+  const int64_t traffic_cap = K / (60 * T);
+  S = S < traffic_cap ? S : traffic_cap;
+  if (S < 2) return p;
+  p.S = (int)S;
+  p.partial_bytes = S * T * O * 4;
+  return p;
+}
+
 }  // namespace
+
+int64_t linear_workspace_bytes(int64_t T, int64_t O, int64_t K) {
+  const SplitPlan p = split_plan(T, O, K);
+  return p.S > 1 ? p.partial_bytes : 0;
+}
+
+hipError_t launch_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                            const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,
+                            int64_t O, int64_t K, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                            hipStream_t stream) {
+  const SplitPlan p = split_plan(T, O, K);
+  if (p.S < 2 || !workspace || workspace_bytes < p.partial_bytes)
+    return launch_linear(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K, y, ldy, stream);
+  const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K);
+  float* partials = static_cast<float*>(workspace);
+  hipLaunchKernelGGL((linear_split_kernel<SmallTile>), dim3(p.tiles_total * p.S), dim3(kThreads), 0, stream, op, T,
+                     p.tiles_m, p.tiles_total, p.S, partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((T * O + 255) / 256)), dim3(256), 0, stream, partials,
+                     p.S, T, O, y, ldy);
+  return hipGetLastError();
+}
 
 hipError_t launch_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
                          const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,

@@ -79,6 +79,26 @@ int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_
       sharq::launch_linear(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K, y, ldy, stream));
 }
 
+int64_t sharq_linear_workspace_bytes(int64_t T, int64_t O, int64_t K) {
+  if (T < 0 || O < 0 || K <= 0 || K % 32 != 0) return 0;
+  if (T >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return 0;
+  return sharq::linear_workspace_bytes(T, O, K);
+}
+
+int sharq_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                    const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T, int64_t O,
+                    int64_t K, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  if (T < 0 || O < 0 || K <= 0 || K % 32 != 0 || ldy < O || workspace_bytes < 0) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (T == 0 || O == 0) return SHARQ_OK;
+  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !w_codes || !w_scales || !y) return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
+      !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y) || (workspace && !aligned16(workspace)))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_linear_ws(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K,
+                                            y, ldy, workspace, workspace_bytes, stream));
+}
+
 int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
                          const uint8_t* res_scales, int64_t T_src, const int32_t* a_rows, const int32_t* seg_offsets,
                          int32_t E, const uint8_t* w_codes, const uint8_t* w_scales, int64_t P, int64_t O, int64_t K,

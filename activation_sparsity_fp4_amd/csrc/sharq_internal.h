@@ -17,6 +17,13 @@ hipError_t launch_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, cons
                          const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
                          int64_t T, int64_t O, int64_t K, float* y, int64_t ldy, hipStream_t stream);
 
+int64_t linear_workspace_bytes(int64_t T, int64_t O, int64_t K);
+
+hipError_t launch_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                            const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,
+                            int64_t O, int64_t K, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                            hipStream_t stream);
+
 hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales,
                                  const uint8_t* res_codes, const uint8_t* res_scales,
                                  const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,

@@ -127,6 +127,31 @@ SHARQ_API int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales,
                  hipStream_t stream);
 
 /*
+ * sharq_linear_workspace_bytes -- host. Bytes of device workspace with which
+ * sharq_linear_ws splits K for a (T, O, K) problem, or 0 when it would not
+ * split (then sharq_linear_ws needs no workspace). Invalid shapes give 0.
+ */
+SHARQ_API int64_t sharq_linear_workspace_bytes(int64_t T, int64_t O, int64_t K);
+
+/*
+ * sharq_linear_ws -- sharq_linear (same arguments, same result up to the
+ * accumulation order) that may split K across workgroups when the output has
+ * too few tiles to fill the GPU (decode-sized T, small layers). Each split
+ * writes its fp32 partial tile into the workspace and a second kernel sums
+ * the partials in split order, so calls are deterministic.
+ *  workspace  device memory of at least sharq_linear_workspace_bytes(T, O, K)
+ *             bytes, 16-byte aligned; its contents need no initialisation
+ *             and are overwritten. Calls that may overlap in time need
+ *             separate workspaces. With NULL or a smaller workspace the call
+ *             runs exactly as sharq_linear.
+ */
+SHARQ_API int sharq_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                    const uint8_t* res_codes, const uint8_t* res_scales,
+                    const uint8_t* w_codes, const uint8_t* w_scales,
+                    int64_t T, int64_t O, int64_t K, float* y, int64_t ldy,
+                    void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * sharq_linear_grouped -- sharq_linear per expert segment, for mixture-of-
  * experts layers (SharQ page, Abstract: MoE models are among the targets).
  * Output row p (0 <= p < P) belongs to the expert e with

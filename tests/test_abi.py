@@ -154,3 +154,25 @@ def test_linear_silu_prepare_validation():
     assert fused(h=G + 2) == _lib.SHARQ_EALIGN
     assert fused(hmask=F + 8) == _lib.SHARQ_EALIGN
     assert fused(T=1 << 20, K=1 << 12) == _lib.SHARQ_ENOTIMPL  # activation codes past 32-bit offsets
+
+
+def test_linear_ws_validation():
+    args = (A, B, C, D, E_, F)
+    assert _lib.call("sharq_linear_ws", *args, 0, 8, 64, G, 8, 0, 0, 0) == _lib.SHARQ_OK      # T = 0
+    assert _lib.call("sharq_linear_ws", *args, 4, 8, 48, G, 8, 0, 0, 0) == _lib.SHARQ_EINVAL  # K % 32
+    assert _lib.call("sharq_linear_ws", *args, 4, 8, 64, G, 4, 0, 0, 0) == _lib.SHARQ_EINVAL  # ldy < O
+    assert _lib.call("sharq_linear_ws", *args, 4, 8, 64, G, 8, 0, -1, 0) == _lib.SHARQ_EINVAL  # workspace bytes
+    assert _lib.call("sharq_linear_ws", *args, 4, 8, 64, G, 8, A + 8, 1024, 0) == _lib.SHARQ_EALIGN
+    assert _lib.call("sharq_linear_ws", A, B, C, D, E_, 0, 4, 8, 64, G, 8, 0, 0, 0) == _lib.SHARQ_EINVAL
+
+
+def test_linear_workspace_bytes():
+    ws = lambda T, O, K: _lib.call("sharq_linear_workspace_bytes", T, O, K)
+    assert ws(2048, 28672, 4096) == 0        # enough tiles: no split
+    assert ws(8, 4096, 96) == 0              # K % 128 != 0: no split
+    assert ws(4, 8, 48) == 0                 # invalid shape
+    # decode down projection: 32 column tiles, 16 splits of 14 stages, partials [16][1][8192] fp32
+    assert ws(1, 8192, 28672) == 16 * 1 * 8192 * 4
+    # at T = 64 the partials' traffic caps the splits at K / (60 T) = 7
+    assert ws(64, 8192, 28672) == 7 * 64 * 8192 * 4
+    assert ws(128, 4096, 4096) == 0          # the cap allows no split

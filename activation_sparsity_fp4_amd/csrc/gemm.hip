@@ -864,8 +864,10 @@ void launch_tiles(const Operands& op, int64_t T, float* y, int64_t ldy, hipStrea
 // Split-K plan: problems with at most 256 rows and fewer 128 x 256 tiles
 // than two per CU (and K long enough) split K so that about two workgroups
 // per CU take part, each over at least 4 stages, at most 16 splits, and with
-// the partials' traffic (written and read once: 8 S T O bytes) at most a
-// quarter of the weight's (O K 17/32 bytes), i.e. S <= K / (60 T).
+// the partials (4 S T O bytes, written once and read once) at most the
+// larger of a quarter of the weight's bytes (O K 17/32) and 32 MB: a small
+// layer is latency-bound and gains from the parallelism even when the
+// partials outweigh its weight.
 constexpr int64_t kSplitMaxRows = 256;
 
 struct SplitPlan {
@@ -883,7 +885,9 @@ SplitPlan split_plan(int64_t T, int64_t O, int64_t K) {
   int64_t S = kTwoPerCu / p.tiles_total;
   S = S < nsteps / 4 ? S : nsteps / 4;
   S = S < kMaxSplits ? S : kMaxSplits;
-  const int64_t traffic_cap = K / (60 * T);
+  const int64_t w_bytes = O * K * 17 / 32;
+  const int64_t cap_bytes = w_bytes / 4 > ((int64_t)32 << 20) ? w_bytes / 4 : ((int64_t)32 << 20);
+  const int64_t traffic_cap = cap_bytes / (4 * T * O);
   S = S < traffic_cap ? S : traffic_cap;
   if (S < 2) return p;
   p.S = (int)S;

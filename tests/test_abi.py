@@ -173,6 +173,7 @@ def test_linear_workspace_bytes():
     assert ws(4, 8, 48) == 0                 # invalid shape
     # decode down projection: 32 column tiles, 16 splits of 14 stages, partials [16][1][8192] fp32
     assert ws(1, 8192, 28672) == 16 * 1 * 8192 * 4
-    # at T = 64 the partials' traffic caps the splits at K / (60 T) = 7
-    assert ws(64, 8192, 28672) == 7 * 64 * 8192 * 4
-    assert ws(128, 4096, 4096) == 0          # the cap allows no split
+    assert ws(64, 8192, 28672) == 16 * 64 * 8192 * 4
+    # 128 x 4096 layer: 16 tiles, 8 splits of 4 stages each
+    assert ws(128, 4096, 4096) == 8 * 128 * 4096 * 4
+    assert ws(300, 4096, 4096) == 0          # more rows than the split path takes

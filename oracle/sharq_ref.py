@@ -56,6 +56,10 @@ __all__ = [
     "E2M1_GRID",
     "bf16_bits_to_f32",
     "f64_to_bf16_bits_rne",
+    "f32_to_bf16_bits_rne",
+    "rms_sum_sq_ref",
+    "rms_row_scale_ref",
+    "rms_normalize_ref",
     "absorb_gamma",
     "select_nm",
     "floor_log2_f32",
@@ -111,6 +115,86 @@ def f64_to_bf16_bits_rne(h: np.ndarray) -> np.ndarray:
     r = np.ldexp(np.rint(np.ldexp(m, 8)), ex - 8)  # exact in float64
     r32 = r.astype(np.float32)  # exact: r has 8 significant bits
     return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def f32_to_bf16_bits_rne(v32: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16, ties to the even significand.
+
+    Written from the bf16 grid: in the binade of v (exponent e = floor(log2|v|))
+    bf16 values are spaced 2**(e - 7), and below 2**-126 (the subnormal range)
+    uniformly 2**-133; v / spacing is rounded half-to-even by numpy's ``rint``
+    and scaled back, exactly, in float64. Finite inputs whose rounding stays
+    finite in bf16 only.
+    """
+    v = np.asarray(v32, dtype=np.float32).astype(np.float64)
+    _require_finite(v, "f32_to_bf16_bits_rne")
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))  # a = f * 2**ex, f in [0.5, 1): e = ex - 1
+    step_exp = np.maximum(ex - 1 - 7, -133)
+    r = np.ldexp(np.rint(np.ldexp(v, -step_exp)), step_exp)
+    r32 = r.astype(np.float32)  # exact: r lies on the bf16 grid
+    _require_finite(r32, "bf16 rounding")
+    return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# O0: full RMSNorm absorption (the norm step right before the path: [SharQ]
+# Abstract, the fused prepare absorbs the layer norm). Reading: the model's
+# RMSNorm, x_n = bf16(x * r) with r = 1 / sqrt(mean_k x_k**2 + eps) per row,
+# then x' = x_n * gamma; the row's sum of squares is accumulated in float64 in
+# a fixed order so that every implementation that follows the order gets the
+# same bits.
+# ---------------------------------------------------------------------------
+
+def rms_sum_sq_ref(x_bits: np.ndarray) -> np.ndarray:
+    """S = sum_k x_k**2 per row in float64, in this fixed order.
+
+    Each square of a bf16 value is exact in float64. The 32 squares of each MX
+    block are added in index order, one after the other, starting from 0; the
+    block sums are then combined by a pairwise tree over blocks in index order
+    (adjacent pairs (2i, 2i + 1), level by level), padded with zero blocks to a
+    power of two.
+    """
+    x = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16)).astype(np.float64)
+    _require_finite(x, "x")
+    T, K = x.shape
+    if K % BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    nb = K // BLOCK
+    sq = (x * x).reshape(T, nb, BLOCK)
+    blk = np.zeros((T, nb))
+    for k in range(BLOCK):
+        blk = blk + sq[:, :, k]
+    npad = 1
+    while npad < nb:
+        npad *= 2
+    tree = np.zeros((T, npad))
+    tree[:, :nb] = blk
+    while tree.shape[1] > 1:
+        tree = tree[:, 0::2] + tree[:, 1::2]
+    return tree[:, 0]
+
+
+def rms_row_scale_ref(x_bits: np.ndarray, eps: float) -> np.ndarray:
+    """Per-row RMSNorm scale r = fp32(1 / sqrt(S / K + eps)), eps > 0, with S
+    from ``rms_sum_sq_ref``. The mean, the addition of eps (taken exactly from
+    its float32 value), sqrt and the reciprocal are float64 operations, each
+    correctly rounded; r is then rounded to float32."""
+    eps = float(np.float32(eps))
+    if not (eps > 0 and np.isfinite(eps)):
+        raise ValueError("eps must be finite and > 0")
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    v = rms_sum_sq_ref(x_bits) / x_bits.shape[1] + eps
+    return (1.0 / np.sqrt(v)).astype(np.float32)
+
+
+def rms_normalize_ref(x_bits: np.ndarray, eps: float) -> tuple[np.ndarray, np.ndarray]:
+    """x_n = bf16_rne(fp32(x) * r) per row: returns (x_n bf16 bits [T, K], r [T])."""
+    r = rms_row_scale_ref(x_bits, eps)
+    x32 = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16))
+    with np.errstate(under="ignore"):
+        xr = (x32 * r[:, None]).astype(np.float32)
+    return f32_to_bf16_bits_rne(xr), r
 
 
 def absorb_gamma(x_bits: np.ndarray, gamma_bits: np.ndarray | None) -> np.ndarray:
@@ -294,18 +378,24 @@ def unpack_mask(mask_bytes: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def prepare_ref(x_bits: np.ndarray, gamma_bits: np.ndarray | None, n: int, m: int,
-                keep_intermediates: bool = False) -> dict:
+                keep_intermediates: bool = False, rms_eps: float | None = None) -> dict:
     """Oracle of the fused prepare operator on a [T, K] bf16 activation.
 
     Returns packed outputs ``mask`` [T,K/8], ``bb_codes`` [T,K/2],
     ``bb_scales`` [T,K/32], ``res_codes`` [T,K/2], ``res_scales`` [T,K/32]
-    (all uint8). With ``keep_intermediates`` it also returns x', the boolean
-    mask, the dequantised backbone q, the residual r and the unpacked codes.
+    (all uint8). With ``rms_eps`` the full RMSNorm is absorbed first (O0:
+    x is replaced by bf16(x * r), r returned as ``rms_scale`` float32 [T]).
+    With ``keep_intermediates`` it also returns x', the boolean mask, the
+    dequantised backbone q, the residual r and the unpacked codes.
     """
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     T, K = x_bits.shape
     if K % BLOCK or K % m:
         raise ValueError("K must be a multiple of 32 and of m")
+    # O0
+    rms = None
+    if rms_eps is not None:
+        x_bits, rms = rms_normalize_ref(x_bits, rms_eps)
     # O1
     xp = absorb_gamma(x_bits, gamma_bits)
     # O2
@@ -325,6 +415,8 @@ def prepare_ref(x_bits: np.ndarray, gamma_bits: np.ndarray | None, n: int, m: in
         "res_codes": pack_nibbles(rs_c),
         "res_scales": (rs_e + 127).astype(np.uint8),
     }
+    if rms is not None:
+        out["rms_scale"] = rms
     if keep_intermediates:
         out.update(xp=xp, keep=keep, q=q, r=r, bb_c=bb_c, bb_e=bb_e, rs_c=rs_c, rs_e=rs_e)
     return out

@@ -44,6 +44,7 @@ class Prepared(NamedTuple):
     res_scales: "object"  # [G, T, 4]
     mask: "object"        # [T, K/8] (row-major bitmap) or None
     K: int
+    rms_scale: "object" = None  # fp32 [T] per-row 1/rms when the RMSNorm was absorbed
 
 
 class MXFP4(NamedTuple):
@@ -103,8 +104,11 @@ def _check_prepared(prep):
     _check_stage_major(prep.res_codes, prep.res_scales, T, prep.K, "residual")
 
 
-def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: Optional[Prepared] = None) -> Prepared:
-    """Fused prepare: N:M mask, MXFP4 backbone, residual against it, MXFP4 residual."""
+def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: Optional[Prepared] = None,
+            rms_eps: Optional[float] = None) -> Prepared:
+    """Fused prepare: N:M mask, MXFP4 backbone, residual against it, MXFP4 residual.
+    With rms_eps the whole RMSNorm (per-row 1/rms, then gamma) is absorbed
+    first; the per-row scales are returned in ``rms_scale``."""
     torch = _torch()
     _need(x, torch.bfloat16, "x", 2)
     if x.stride(1) != 1:
@@ -118,9 +122,18 @@ def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: 
         G = stages(K)
         out = Prepared(torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
                        torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
-                       torch.empty((T, K // 8), **kw) if with_mask else None, K)
+                       torch.empty((T, K // 8), **kw) if with_mask else None, K,
+                       torch.empty((T,), dtype=torch.float32, device=x.device) if rms_eps is not None else None)
     elif out.K != K:
         raise ValueError("out was allocated for another K")
+    if rms_eps is not None:
+        if out.rms_scale is None:
+            raise ValueError("out has no rms_scale buffer")
+        st = _lib.call("sharq_prepare_rms", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), float(rms_eps), n, m,
+                       out.rms_scale.data_ptr(), out.bb_codes.data_ptr(), out.bb_scales.data_ptr(),
+                       out.res_codes.data_ptr(), out.res_scales.data_ptr(), _ptr(out.mask), _stream(x.device))
+        _lib.check("sharq_prepare_rms", st)
+        return out
     st = _lib.call("sharq_prepare", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), n, m,
                    out.bb_codes.data_ptr(), out.bb_scales.data_ptr(), out.res_codes.data_ptr(),
                    out.res_scales.data_ptr(), _ptr(out.mask), _stream(x.device))

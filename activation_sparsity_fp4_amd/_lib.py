@@ -28,6 +28,8 @@ SIGNATURES = {
     "sharq_status_string": (ctypes.c_char_p, [_INT]),
     "sharq_abi_version": (_INT, []),
     "sharq_prepare": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _INT, _P, _P, _P, _P, _P, _P]),
+    "sharq_prepare_rms": (_INT, [_P, _I64, _I64, _I64, _P, ctypes.c_float, _INT, _INT, _P, _P, _P, _P, _P, _P,
+                                 _P]),
     "sharq_quantize_mxfp4": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "sharq_linear": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "sharq_linear_workspace_bytes": (_I64, [_I64, _I64, _I64]),

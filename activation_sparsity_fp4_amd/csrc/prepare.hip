@@ -49,6 +49,68 @@ __device__ __forceinline__ BlockOfLane block_of_lane(uint32_t stages, uint32_t b
   return r;
 }
 
+// bf16 bits of a float32 value, rounded to nearest, ties to even (finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void load_block(const uint16_t* p, uint4 (&raw)[4]) {
+  const uint4* src = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = src[i];
+}
+
+__device__ __forceinline__ void widen_block(const uint4 (&raw)[4], float (&xv)[32]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xv[8 * i + 2 * j] = bf16_lo(w[j]);
+      xv[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+    }
+  }
+}
+
+// x' = x * gamma on one block, then selection, quantisation and the stores.
+template <int N, int M, bool kGamma>
+__device__ __forceinline__ void prepare_store(float (&xv)[32], const uint16_t* __restrict__ gamma, uint32_t t,
+                                              uint32_t b, uint32_t blocks_per_row, uint32_t rows,
+                                              uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_scales,
+                                              uint8_t* __restrict__ res_codes, uint8_t* __restrict__ res_scales,
+                                              uint8_t* __restrict__ mask_out) {
+  if constexpr (kGamma) {
+    uint4 graw[4];
+    load_block(gamma + (int64_t)b * kBlock, graw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w[4] = {graw[i].x, graw[i].y, graw[i].z, graw[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[8 * i + 2 * j] *= bf16_lo(w[j]);
+        xv[8 * i + 2 * j + 1] *= bf16_hi(w[j]);
+      }
+    }
+  }
+  const PreparedBlock pb = prepare_block<N, M, kGamma>(xv);
+  *reinterpret_cast<uint4*>(bb_codes + code_offset(t, b, rows)) = pb.c_bb;
+  *reinterpret_cast<uint4*>(res_codes + code_offset(t, b, rows)) = pb.c_rs;
+  bb_scales[scale_index(t, b, rows)] = (uint8_t)pb.e_bb;
+  res_scales[scale_index(t, b, rows)] = (uint8_t)pb.e_rs;
+  if (mask_out) reinterpret_cast<uint32_t*>(mask_out)[(int64_t)t * blocks_per_row + b] = pb.keep;
+}
+
+__device__ __forceinline__ void zero_block(uint32_t t, uint32_t b, uint32_t rows, uint8_t* __restrict__ bb_codes,
+                                           uint8_t* __restrict__ bb_scales, uint8_t* __restrict__ res_codes,
+                                           uint8_t* __restrict__ res_scales) {
+  *reinterpret_cast<uint4*>(bb_codes + code_offset(t, b, rows)) = make_uint4(0, 0, 0, 0);
+  *reinterpret_cast<uint4*>(res_codes + code_offset(t, b, rows)) = make_uint4(0, 0, 0, 0);
+  bb_scales[scale_index(t, b, rows)] = 0;
+  res_scales[scale_index(t, b, rows)] = 0;
+}
+
+// The whole operator without the norm: x' = x (times gamma when given).
 template <int N, int M, bool kGamma>
 __global__ __launch_bounds__(256) void prepare_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma,
@@ -59,55 +121,161 @@ __global__ __launch_bounds__(256) void prepare_kernel(
   const BlockOfLane lb = block_of_lane(stages, blocks_per_row, rows);
   if (!lb.block_ok) {
     // the unused blocks of a last, partial stage are zero
-    if (lb.row_ok) {
-      *reinterpret_cast<uint4*>(bb_codes + code_offset(lb.t, lb.b, rows)) = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(res_codes + code_offset(lb.t, lb.b, rows)) = make_uint4(0, 0, 0, 0);
-      bb_scales[scale_index(lb.t, lb.b, rows)] = 0;
-      res_scales[scale_index(lb.t, lb.b, rows)] = 0;
-    }
+    if (lb.row_ok) zero_block(lb.t, lb.b, rows, bb_codes, bb_scales, res_codes, res_scales);
     return;
   }
-  const uint32_t t = lb.t, b = lb.b;
-  const uint32_t gid = t * blocks_per_row + b;  // row-major block index (mask words)
-
-  // load 32 bf16 (64 B) and widen to fp32
-  const uint4* src = reinterpret_cast<const uint4*>(x + (int64_t)t * ldx + (int64_t)b * kBlock);
   uint4 raw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) raw[i] = src[i];
+  load_block(x + (int64_t)lb.t * ldx + (int64_t)lb.b * kBlock, raw);
   float xv[32];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xv[8 * i + 2 * j] = bf16_lo(w[j]);
-      xv[8 * i + 2 * j + 1] = bf16_hi(w[j]);
-    }
-  }
-  if constexpr (kGamma) {
-    const uint4* gsrc = reinterpret_cast<const uint4*>(gamma + (int64_t)b * kBlock);
+  widen_block(raw, xv);
+  prepare_store<N, M, kGamma>(xv, gamma, lb.t, lb.b, blocks_per_row, rows, bb_codes, bb_scales, res_codes,
+                              res_scales, mask_out);
+}
+
+// Full RMSNorm absorption (page "SharQ: ...", Abstract: the fused prepare
+// absorbs the layer norm): per row r = 1 / sqrt(S / K + eps), then
+// x' = bf16(x * r) (times gamma when given) goes through the same per-block
+// prepare.
+//
+// S, the row's sum of squares, is accumulated in float64 in a fixed order so
+// that r is reproducible bit for bit: the 32 squares of each MX block one
+// after the other in index order (each square of a bf16 value is exact in
+// float64), then the block sums by a pairwise tree over blocks in index order
+// (adjacent pairs, level by level, padded with zero blocks to a power of two).
+// Mean, eps, sqrt and the reciprocal are correctly rounded float64
+// operations; r is rounded to float32.
+//
+// One workgroup (4 waves) owns 4 rows and walks all of K, so x is read from
+// HBM once. A wave step covers a chunk of 16 consecutive blocks of each of
+// the 4 rows (lane l: row l / 16, block 16 * chunk + l % 16); chunks go to the
+// waves round-robin. Pass 1 sums each block and folds the 16 block sums of a
+// row by a shuffle-down tree inside the lane's 16-lane segment, which is the
+// pairwise tree over that aligned chunk. Pass 2 (wave w, row w) folds the
+// chunk sums the same way over 64 lanes per round and combines rounds with a
+// binary-counter stack, which completes the tree. Leaves past the last block
+// add exact zeros (the sums are non-negative), so padding further than the
+// next power of two changes nothing. Pass 3 prepares the blocks; the first
+// kHold chunks of each wave stay in registers from pass 1, later ones are
+// read again (the workgroup's own rows, still in L2).
+constexpr int kRmsRows = 4;
+constexpr uint32_t kRmsMaxChunks = 256;  // K <= 131072
+constexpr int kRmsHold = 2;
+
+template <int N, int M, bool kGamma>
+__global__ __launch_bounds__(256) void prepare_rms_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma, uint32_t K, uint32_t rows,
+    float eps, float* __restrict__ r_out, uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_scales,
+    uint8_t* __restrict__ res_codes, uint8_t* __restrict__ res_scales, uint8_t* __restrict__ mask_out) {
+  __shared__ double chunk_sum[kRmsRows][kRmsMaxChunks];
+  __shared__ float r_row[kRmsRows];
+  const uint32_t wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t t = blockIdx.x * kRmsRows + (lane >> 4);
+  const bool row_ok = t < rows;
+  const uint32_t nb = K / kBlock, nblk_padded = (nb + 3) & ~3u, nchunks = (nb + 15) / 16;
+  const uint16_t* xrow = x + (int64_t)(row_ok ? t : 0) * ldx;
+
+  auto chunk_block = [&](uint32_t c) { return c * 16 + (lane & 15); };
+  auto fold_chunk = [&](uint32_t c, const uint4 (&raw)[4]) {
+    double s = 0.0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4 gr = gsrc[i];
-      const uint32_t w[4] = {gr.x, gr.y, gr.z, gr.w};
+      const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        xv[8 * i + 2 * j] *= bf16_lo(w[j]);
-        xv[8 * i + 2 * j + 1] *= bf16_hi(w[j]);
+        const double lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+        s = s + lo * lo;  // the product is exact, so a fused multiply-add rounds the same way
+        s = s + hi * hi;
       }
     }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) s = s + __shfl_down(s, d, 16);
+    if ((lane & 15) == 0) chunk_sum[lane >> 4][c] = s;
+  };
+  auto load_chunk = [&](uint32_t c, uint4 (&raw)[4]) {
+    const uint32_t b = chunk_block(c);
+    if (row_ok && b < nb) {
+      load_block(xrow + (int64_t)b * kBlock, raw);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) raw[i] = make_uint4(0, 0, 0, 0);  // squares of zero: exact zeros
+    }
+  };
+
+  // pass 1: block sums, folded per chunk
+  uint4 held[kRmsHold][4];
+#pragma unroll
+  for (int it = 0; it < kRmsHold; ++it) {
+    const uint32_t c = wave + 4 * it;
+    if (c < nchunks) {
+      load_chunk(c, held[it]);
+      fold_chunk(c, held[it]);
+    }
   }
+  for (uint32_t c = wave + 4 * kRmsHold; c < nchunks; c += 4) {
+    uint4 raw[4];
+    load_chunk(c, raw);
+    fold_chunk(c, raw);
+  }
+  __syncthreads();
 
-  const PreparedBlock pb = prepare_block<N, M, kGamma>(xv);
-  const uint4 c_bb = pb.c_bb, c_rs = pb.c_rs;
-  const uint32_t e_bb = pb.e_bb, e_rs = pb.e_rs, keep = pb.keep;
+  // pass 2: wave w completes the tree of row w
+  {
+    const uint32_t rounds = (nchunks + 63) / 64;
+    uint32_t npad = 1;
+    while (npad < rounds) npad <<= 1;
+    double stack[3];
+    double root = 0.0;
+    for (uint32_t rd = 0; rd < npad; ++rd) {
+      const uint32_t c = rd * 64 + lane;
+      double s = c < nchunks ? chunk_sum[wave][c] : 0.0;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) s = s + __shfl_down(s, d, 64);
+      double cur = __shfl(s, 0, 64);
+#pragma unroll
+      for (int l = 0; l < 3; ++l) {
+        if ((rd >> l) & 1u) {
+          cur = stack[l] + cur;
+        } else {
+          stack[l] = cur;
+          break;
+        }
+      }
+      root = cur;
+    }
+    if (lane == 0) {
+      const float r = (float)(1.0 / sqrt(root / (double)K + (double)eps));
+      r_row[wave] = r;
+      const uint32_t tw = blockIdx.x * kRmsRows + wave;
+      if (tw < rows) r_out[tw] = r;
+    }
+  }
+  __syncthreads();
 
-  *reinterpret_cast<uint4*>(bb_codes + code_offset(t, b, rows)) = c_bb;
-  *reinterpret_cast<uint4*>(res_codes + code_offset(t, b, rows)) = c_rs;
-  bb_scales[scale_index(t, b, rows)] = (uint8_t)e_bb;
-  res_scales[scale_index(t, b, rows)] = (uint8_t)e_rs;
-  if (mask_out) reinterpret_cast<uint32_t*>(mask_out)[gid] = keep;
+  // pass 3: prepare bf16(x * r)
+  const float r = r_row[lane >> 4];
+  auto emit = [&](uint32_t c, const uint4 (&raw)[4]) {
+    const uint32_t b = chunk_block(c);
+    if (!row_ok || b >= nblk_padded) return;
+    if (b >= nb) {
+      zero_block(t, b, rows, bb_codes, bb_scales, res_codes, res_scales);  // partial last stage
+      return;
+    }
+    float xv[32];
+    widen_block(raw, xv);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) xv[k] = __uint_as_float(f32_to_bf16_rne(xv[k] * r) << 16);
+    prepare_store<N, M, kGamma>(xv, gamma, t, b, nb, rows, bb_codes, bb_scales, res_codes, res_scales, mask_out);
+  };
+#pragma unroll
+  for (int it = 0; it < kRmsHold; ++it) {
+    const uint32_t c = wave + 4 * it;
+    if (c < nchunks) emit(c, held[it]);
+  }
+  for (uint32_t c = wave + 4 * kRmsHold; c < nchunks; c += 4) {
+    uint4 raw[4];
+    load_chunk(c, raw);
+    emit(c, raw);
+  }
 }
 
 // Plain MXFP4 coding of bf16 rows (the weight quantiser): same element and
@@ -150,17 +318,30 @@ static inline uint64_t lanes_for(int64_t T, int64_t K) {
 }
 
 hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma,
-                          int n, int m, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
-                          uint8_t* res_scales, uint8_t* mask, hipStream_t stream) {
+                          float rms_eps, float* rms_scale, int n, int m, uint8_t* bb_codes, uint8_t* bb_scales,
+                          uint8_t* res_codes, uint8_t* res_scales, uint8_t* mask, hipStream_t stream) {
+  if (rms_scale) {
+    const dim3 grid((unsigned)((T + kRmsRows - 1) / kRmsRows)), block(256);
+#define SHARQ_PREP_RMS(NN, MM, GG)                                                                          \
+  hipLaunchKernelGGL((prepare_rms_kernel<NN, MM, GG>), grid, block, 0, stream, x, ldx, gamma, (uint32_t)K, \
+                     (uint32_t)T, rms_eps, rms_scale, bb_codes, bb_scales, res_codes, res_scales, mask)
+    if (n == 2 && m == 4) {
+      if (gamma) SHARQ_PREP_RMS(2, 4, true); else SHARQ_PREP_RMS(2, 4, false);
+    } else {
+      if (gamma) SHARQ_PREP_RMS(8, 16, true); else SHARQ_PREP_RMS(8, 16, false);
+    }
+#undef SHARQ_PREP_RMS
+    return hipGetLastError();
+  }
   const uint32_t bpr = (uint32_t)(K / kBlock);
   const uint32_t stages = (uint32_t)((K + 127) / 128);
   const uint64_t lanes = lanes_for(T, K);
   // small problems: one wave per workgroup so that more CUs take part
   const unsigned threads = lanes >= (1u << 18) ? 256 : 64;
   const dim3 grid((unsigned)((lanes + threads - 1) / threads)), block(threads);
-#define SHARQ_PREP(NN, MM, GG)                                                              \
-  hipLaunchKernelGGL((prepare_kernel<NN, MM, GG>), grid, block, 0, stream, x, ldx, gamma,   \
-                     bpr, stages, (uint32_t)T, bb_codes, bb_scales, res_codes, res_scales, mask)
+#define SHARQ_PREP(NN, MM, GG)                                                                                \
+  hipLaunchKernelGGL((prepare_kernel<NN, MM, GG>), grid, block, 0, stream, x, ldx, gamma, bpr, stages, (uint32_t)T, \
+                     bb_codes, bb_scales, res_codes, res_scales, mask)
   if (n == 2 && m == 4) {
     if (gamma) SHARQ_PREP(2, 4, true); else SHARQ_PREP(2, 4, false);
   } else {

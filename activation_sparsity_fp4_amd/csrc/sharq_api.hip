@@ -1,6 +1,8 @@
 // C ABI of the SharQ library: host-side argument validation (before any HIP
 // call) and dispatch to the kernel launchers.
 
+#include <math.h>
+
 #include "../../include/sharq.h"
 #include "sharq_internal.h"
 
@@ -51,8 +53,25 @@ int sharq_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const ui
   if (!aligned16(x) || (gamma && !aligned16(gamma)) || !aligned16(bb_codes) || !aligned16(bb_scales) ||
       !aligned16(res_codes) || !aligned16(res_scales) || (mask && !aligned16(mask)))
     return SHARQ_EALIGN;
-  return hip_status(sharq::launch_prepare(x, T, K, ldx, gamma, n, m, bb_codes, bb_scales, res_codes, res_scales,
-                                          mask, stream));
+  return hip_status(sharq::launch_prepare(x, T, K, ldx, gamma, 0.0f, nullptr, n, m, bb_codes, bb_scales, res_codes,
+                                          res_scales, mask, stream));
+}
+
+int sharq_prepare_rms(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma, float eps,
+                      int n, int m, float* rms_scale, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
+                      uint8_t* res_scales, uint8_t* mask, hipStream_t stream) {
+  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
+  const int rc = check_rows(T, K, ldx);
+  if (rc != SHARQ_OK) return rc;
+  if (K % m != 0 || !(eps > 0.0f) || !(eps < INFINITY)) return SHARQ_EINVAL;
+  if (K / 32 > 4096) return SHARQ_ENOTIMPL;  // the row-sum tree holds at most 4096 blocks
+  if (T == 0) return SHARQ_OK;
+  if (!x || !rms_scale || !bb_codes || !bb_scales || !res_codes || !res_scales) return SHARQ_EINVAL;
+  if (!aligned16(x) || (gamma && !aligned16(gamma)) || !aligned16(rms_scale) || !aligned16(bb_codes) ||
+      !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) || (mask && !aligned16(mask)))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_prepare(x, T, K, ldx, gamma, eps, rms_scale, n, m, bb_codes, bb_scales,
+                                          res_codes, res_scales, mask, stream));
 }
 
 int sharq_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, uint8_t* codes, uint8_t* scales,

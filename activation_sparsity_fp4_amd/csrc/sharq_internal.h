@@ -6,9 +6,11 @@
 
 namespace sharq {
 
+// rms_scale == nullptr: no RMSNorm; otherwise r per row is written there and
+// absorbed (rms_eps > 0).
 hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma,
-                          int n, int m, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
-                          uint8_t* res_scales, uint8_t* mask, hipStream_t stream);
+                          float rms_eps, float* rms_scale, int n, int m, uint8_t* bb_codes, uint8_t* bb_scales,
+                          uint8_t* res_codes, uint8_t* res_scales, uint8_t* mask, hipStream_t stream);
 
 hipError_t launch_quantize(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, uint8_t* codes,
                            uint8_t* scales, hipStream_t stream);

@@ -2,9 +2,9 @@
 """Benchmark of the SharQ linear hot path on one MI355X.
 
 Default workload: a Llama-3.1-8B-shaped MLP block at 2048-token prefill, 2:4,
-MXFP4, RMSNorm gamma absorbed in the first prepare:
-    prepare(x, gamma) -> two-path GEMM gate|up [28672 x 4096] -> silu_mul
-    -> prepare(h) -> two-path GEMM down [4096 x 14336]
+MXFP4, the RMSNorm (per-row 1/rms and gamma) absorbed in the first prepare:
+    prepare(rmsnorm(x)) -> fused [two-path GEMM gate|up [28672 x 4096] ->
+    silu(gate) * up -> prepare(h)] -> two-path GEMM down [4096 x 14336]
 One step = one pass of that chain over 2048 tokens. Inputs are seeded synthetic
 data resident in HBM before the timed region; weights are quantised once on
 the GPU (not timed).
@@ -81,8 +81,9 @@ def build_workload(name, torch, sq, unfused=False):
         x, g = _to_gpu_bf16(torch, wl["x"]), _to_gpu_bf16(torch, wl["gamma"])
         w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"]))
         w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"]))
+        eps = 1e-5  # Llama-3.1 RMSNorm epsilon
         buf = {}
-        buf["p1"] = sq.prepare(x, g, 2, 4)
+        buf["p1"] = sq.prepare(x, g, 2, 4, rms_eps=eps)
         fa1, fe1 = gemm_flops(T, 2 * I, H)
         fa2, fe2 = gemm_flops(T, H, I)
         if unfused:
@@ -104,19 +105,20 @@ def build_workload(name, torch, sq, unfused=False):
                       fused_bytes(T, I, H), fa1, fe1),
             ]
         buf["y"] = sq.linear(buf["p2"], w_dn)
-        stages = [Stage("prepare_x_gamma", lambda: sq.prepare(x, g, 2, 4, out=buf["p1"]), "hbm",
-                        prepare_bytes(T, H, True))] + middle + [
+        stages = [Stage("prepare_x_rmsnorm", lambda: sq.prepare(x, g, 2, 4, out=buf["p1"], rms_eps=eps), "hbm",
+                        prepare_bytes(T, H, True) + 4 * T)] + middle + [
             Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "mfma", gemm_bytes(T, H, I), fa2, fe2),
         ]
-        cfg = {"workload": "Llama-3.1-8B MLP block, 2048-token prefill, 2:4, MXFP4, RMSNorm gamma absorbed",
-               "tokens": T, "hidden": H, "intermediate": I, "nm": "2:4", "seed": 1002,
+        cfg = {"workload": "Llama-3.1-8B MLP block, 2048-token prefill, 2:4, MXFP4, RMSNorm (1/rms and gamma) "
+                           "absorbed in the first prepare",
+               "tokens": T, "hidden": H, "intermediate": I, "nm": "2:4", "rms_eps": eps, "seed": 1002,
                "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)"}
 
         def oracle_sample(rows):
             from oracle import linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref
             xs = wl["x"][:rows]
             t0 = time.perf_counter()
-            p1 = prepare_ref(xs, wl["gamma"], 2, 4)
+            p1 = prepare_ref(xs, wl["gamma"], 2, 4, rms_eps=1e-5)
             wc, ws = quantize_weight_ref(wl["w_gu"])
             gu, _ = linear_ref(p1["bb_codes"], p1["bb_scales"], p1["res_codes"], p1["res_scales"], wc, ws)
             h = silu_mul_ref(gu.astype(np.float32), I)
@@ -215,17 +217,22 @@ def build_workload(name, torch, sq, unfused=False):
     raise SystemExit(f"unknown workload {name}; choose from {WORKLOADS}")
 
 
-KERNEL_SOURCES = {"gemm": "gemm.hip", "prepare": "prepare.hip", "silu": "glue.hip", "grouped": "gemm.hip"}
+KERNEL_SOURCES = {"gemm": ["gemm.hip"], "prepare": ["prepare.hip"], "silu": ["glue.hip", "silu.h"],
+                  "grouped": ["gemm.hip"]}
+SHARED_HEADERS = ["sharq_device.h", "prepare_block.h", "sort_network.h", "silu.h"]
 
 
 def source_digest(stage_name):
-    """sha256 of the HIP source that implements a stage (ties recorded counters to a kernel version)."""
+    """sha256 over the HIP sources that implement a stage and the device headers
+    they include (ties recorded counters to a kernel version)."""
     import hashlib
     key = "gemm" if "gemm" in stage_name or "grouped" in stage_name else (
         "silu" if "silu" in stage_name else "prepare")
-    path = os.path.join(ROOT, "activation_sparsity_fp4_amd", "csrc", KERNEL_SOURCES[key])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[key] + SHARED_HEADERS:
+        with open(os.path.join(ROOT, "activation_sparsity_fp4_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def recorded_traffic(workload, stage_name):

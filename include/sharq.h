@@ -98,6 +98,28 @@ SHARQ_API int sharq_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx
                   uint8_t* mask, hipStream_t stream);
 
 /*
+ * sharq_prepare_rms -- sharq_prepare with the whole RMSNorm absorbed (SharQ
+ * page, Abstract: the fused prepare operator absorbs the layer norm): per row
+ *   r = fp32(1 / sqrt(S / K + eps)),  x_n = bf16_rne(fp32(x) * r),
+ *   x' = x_n * gamma (fp32; gamma may be NULL),
+ * then the prepare operator on x'. S, the row's sum of squares, is summed in
+ * float64 in a fixed order: the 32 squares of each MX block one after the
+ * other in index order, then the block sums by a pairwise tree over blocks in
+ * index order (adjacent pairs, level by level, padded with zero blocks to a
+ * power of two); mean, eps, sqrt and reciprocal are correctly rounded float64
+ * operations. Two kernels run: the row scales, then the prepare.
+ *  eps        > 0 and finite.
+ *  rms_scale  fp32 [T], written with r (required).
+ *  other arguments as sharq_prepare. Requires K / 32 <= 4096
+ *  (SHARQ_ENOTIMPL otherwise).
+ */
+SHARQ_API int sharq_prepare_rms(const uint16_t* x, int64_t T, int64_t K, int64_t ldx,
+                      const uint16_t* gamma, float eps, int n, int m, float* rms_scale,
+                      uint8_t* bb_codes, uint8_t* bb_scales,
+                      uint8_t* res_codes, uint8_t* res_scales,
+                      uint8_t* mask, hipStream_t stream);
+
+/*
  * sharq_quantize_mxfp4 -- plain MXFP4 of bf16 rows along K (no mask, no
  * residual), the same element and scale rules as sharq_prepare. Used to
  * produce the pre-quantised weight [O][K] that sharq_linear reads.

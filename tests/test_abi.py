@@ -177,3 +177,21 @@ def test_linear_workspace_bytes():
     # 128 x 4096 layer: 16 tiles, 8 splits of 4 stages each
     assert ws(128, 4096, 4096) == 8 * 128 * 4096 * 4
     assert ws(300, 4096, 4096) == 0          # more rows than the split path takes
+
+
+def prep_rms(x=A, T=4, K=64, ldx=64, gamma=0, eps=1e-5, n=2, m=4, rms=G, bc=B, bs=C, rc=D, rs=E_, mask=F):
+    return _lib.call("sharq_prepare_rms", x, T, K, ldx, gamma, eps, n, m, rms, bc, bs, rc, rs, mask, 0)
+
+
+def test_prepare_rms_validation():
+    assert prep_rms(T=0) == _lib.SHARQ_OK
+    assert prep_rms(rms=0) == _lib.SHARQ_EINVAL            # the scales are an output
+    assert prep_rms(eps=0.0) == _lib.SHARQ_EINVAL
+    assert prep_rms(eps=-1.0) == _lib.SHARQ_EINVAL
+    assert prep_rms(eps=float("inf")) == _lib.SHARQ_EINVAL
+    assert prep_rms(eps=float("nan")) == _lib.SHARQ_EINVAL
+    assert prep_rms(n=4, m=8) == _lib.SHARQ_EUNSUPPORTED
+    assert prep_rms(K=48, ldx=48) == _lib.SHARQ_EINVAL
+    assert prep_rms(rms=G + 4) == _lib.SHARQ_EALIGN
+    assert prep_rms(T=1, K=131104, ldx=131104) == _lib.SHARQ_ENOTIMPL  # more than 4096 blocks
+    assert prep_rms(T=0, K=131072, ldx=131072) == _lib.SHARQ_OK

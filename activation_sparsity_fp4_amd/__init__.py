@@ -25,6 +25,7 @@ __all__ = [
     "linear_grouped",
     "linear_silu_prepare",
     "linear_silu_prepare_into",
+    "linear_grouped_silu_prepare",
     "silu_mul",
     "SharqError",
     "status_string",
@@ -290,6 +291,55 @@ def _fused_call(prep, w_gu, T, I, K, n, m, h, hp):
                    _ptr(hp and hp.bb_codes), _ptr(hp and hp.bb_scales), _ptr(hp and hp.res_codes),
                    _ptr(hp and hp.res_scales), _ptr(hp and hp.mask), _stream(prep.bb_codes.device))
     _lib.check("sharq_linear_silu_prepare", st)
+
+
+def linear_grouped_silu_prepare(prep: Prepared, w_gu: MXFP4, seg_offsets, a_rows=None, n: int = 2, m: int = 4,
+                                with_h: bool = False, with_prepared: bool = True, with_mask: bool = True,
+                                out: Prepared = None):
+    """Grouped fused gate|up projection: linear_grouped against each expert's
+    w_gu ([E, G, 2I, 64]: I gate rows, then I up rows), then silu_mul and
+    prepare(h, n, m), in one kernel. Rows are the sorted pairs. Returns
+    (Prepared of h or None, h or None), bit-identical to the three-step chain.
+    `out` (a Prepared of [G_I, P, ...]) receives prepare(h) when given."""
+    torch = _torch()
+    _check_prepared(prep)
+    _need(w_gu.codes, torch.uint8, "w_gu.codes", 4)
+    _need(w_gu.scales, torch.uint8, "w_gu.scales", 4)
+    _need(seg_offsets, torch.int32, "seg_offsets", 1)
+    E, _, O, _ = w_gu.codes.shape
+    K = prep.K
+    if w_gu.K != K or O % 2:
+        raise ValueError("w_gu must be [E, 2I, K] with the activation's K")
+    _check_stage_major(w_gu.codes[0], w_gu.scales[0], O, K, "w_gu")
+    if seg_offsets.numel() != E + 1:
+        raise ValueError("seg_offsets must have E + 1 entries")
+    if a_rows is not None:
+        _need(a_rows, torch.int32, "a_rows", 1)
+        P = a_rows.numel()
+    else:
+        P = prep.bb_codes.shape[1]
+    I = O // 2
+    dev = prep.bb_codes.device
+    kw = dict(dtype=torch.uint8, device=dev)
+    h = torch.empty((P, I), dtype=torch.bfloat16, device=dev) if with_h else None
+    hp = None
+    if out is not None:
+        _check_prepared(out)
+        if out.K != I or out.bb_codes.shape[1] != P:
+            raise ValueError("out must be a Prepared of [P, I]")
+        hp = out
+    elif with_prepared:
+        G = stages(I)
+        hp = Prepared(torch.empty((G, P, 64), **kw), torch.empty((G, P, 4), **kw),
+                      torch.empty((G, P, 64), **kw), torch.empty((G, P, 4), **kw),
+                      torch.empty((P, I // 8), **kw) if with_mask else None, I)
+    st = _lib.call("sharq_linear_grouped_silu_prepare", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
+                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), prep.bb_codes.shape[1], _ptr(a_rows),
+                   seg_offsets.data_ptr(), E, w_gu.codes.data_ptr(), w_gu.scales.data_ptr(), P, I, K, n, m, _ptr(h),
+                   _ptr(hp and hp.bb_codes), _ptr(hp and hp.bb_scales), _ptr(hp and hp.res_codes),
+                   _ptr(hp and hp.res_scales), _ptr(hp and hp.mask), _stream(dev))
+    _lib.check("sharq_linear_grouped_silu_prepare", st)
+    return hp, h
 
 
 def silu_mul(gu, out=None):

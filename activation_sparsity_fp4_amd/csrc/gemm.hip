@@ -674,16 +674,18 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// Grouped two-path GEMM over token-sorted expert segments (128 x 256 tiles).
-// blockIdx.y is a linear index over all (expert, row-tile) pairs; the expert
-// is found by a prefix sum of per-expert tile counts. blockIdx.x is the output
-// column tile.
-template <bool kRingPath>
-__global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) void linear_grouped_kernel(
-    Operands op, const int32_t* __restrict__ a_rows, const int32_t* __restrict__ seg, int E,
-    const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, float* __restrict__ y) {
-  using C = SmallTile;
-  SHARQ_GEMM_LDS(C, kRingPath)
+// Row tile of a grouped launch: blockIdx.y is a linear index over all
+// (expert, row-tile) pairs, expert e holding ceil(count_e / BM) row tiles in
+// expert order; the expert is found by a wave-wide prefix sum of the
+// per-expert tile counts. Returns e = -1 (uniform over the workgroup) for the
+// surplus indices of the grid's upper bound.
+struct GroupedTile {
+  int e;
+  TileRows tr;
+};
+template <class C>
+__device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ seg, int E,
+                                                    const int32_t* __restrict__ a_rows) {
   __shared__ int s_info[2];
   const int tid = threadIdx.x;
   const int target = blockIdx.y;
@@ -705,23 +707,43 @@ __global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) vo
     }
   }
   __syncthreads();
-  const int e = s_info[0];
-  if (e < 0) return;  // uniform across the workgroup
-  TileRows tr;
-  tr.m0 = seg[e] + (int64_t)s_info[1] * C::BM;
-  const int64_t hi = seg[e + 1];
-  tr.rows_valid = hi - tr.m0 < C::BM ? hi - tr.m0 : C::BM;
-  tr.gather = a_rows;
+  GroupedTile g;
+  g.e = s_info[0];
+  if (g.e >= 0) {
+    g.tr.m0 = seg[g.e] + (int64_t)s_info[1] * C::BM;
+    const int64_t hi = seg[g.e + 1];
+    g.tr.rows_valid = hi - g.tr.m0 < C::BM ? hi - g.tr.m0 : C::BM;
+    g.tr.gather = a_rows;
+  }
+  return g;
+}
+
+// Operands of expert e: its weight within the [E][G][O][64] / [E][G][O][4] stack.
+__device__ __forceinline__ void select_expert(Operands& op, int e, const uint8_t* __restrict__ w_codes_all,
+                                              const uint8_t* __restrict__ w_scales_all) {
+  op.w_codes = w_codes_all + (int64_t)e * op.O * kRowBytes * op.nsteps;
+  op.w_scales = w_scales_all + (int64_t)e * op.O * 4 * op.nsteps;
+}
+
+// Grouped two-path GEMM over token-sorted expert segments (128 x 256 tiles);
+// blockIdx.x is the output column tile, blockIdx.y the (expert, row tile).
+template <bool kRingPath>
+__global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) void linear_grouped_kernel(
+    Operands op, const int32_t* __restrict__ a_rows, const int32_t* __restrict__ seg, int E,
+    const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, float* __restrict__ y) {
+  using C = SmallTile;
+  SHARQ_GEMM_LDS(C, kRingPath)
+  const GroupedTile g = grouped_tile<C>(seg, E, a_rows);
+  if (g.e < 0) return;  // uniform across the workgroup
   const int64_t n0 = (int64_t)blockIdx.x * C::BN;
-  op.w_codes = w_codes_all + (int64_t)e * op.O * kRowBytes * op.nsteps;  // [E][G][O][64]
-  op.w_scales = w_scales_all + (int64_t)e * op.O * 4 * op.nsteps;          // [E][G][O][4]
+  select_expert(op, g.e, w_codes_all, w_scales_all);
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring<C>(op, tr, TileCols{n0, 0}, lds, acc, 0, op.nsteps);
+    mainloop_ring<C>(op, g.tr, TileCols{n0, 0}, lds, acc, 0, op.nsteps);
   else
-    mainloop_regs(op, tr, n0, lds, lds + C::kStage, acc);
-  store_tile<C>(acc, y, op.O, tr.m0, tr.rows_valid, n0, op.O);
+    mainloop_regs(op, g.tr, n0, lds, lds + C::kStage, acc);
+  store_tile<C>(acc, y, op.O, g.tr.m0, g.tr.rows_valid, n0, op.O);
 }
 
 // ---------------------------------------------------------------------------
@@ -824,6 +846,26 @@ __global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_k
   zero_acc<C>(acc);
   mainloop_ring<C>(op, tr, TileCols{h0, out.I}, lds, acc, 0, op.nsteps);
   silu_prepare_epilogue<N, M>(acc, lds, tr, h0, out);
+}
+
+// Grouped form of the fused gate|up projection (mixture-of-experts layers):
+// the tile of linear_grouped_kernel's row walk with the fused epilogue;
+// blockIdx.x is the 128-column h tile.
+template <int N, int M>
+__global__ __launch_bounds__(kThreads, SmallTile::kOccupancy) void linear_grouped_silu_prepare_kernel(
+    Operands op, const int32_t* __restrict__ a_rows, const int32_t* __restrict__ seg, int E,
+    const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, HOutputs out) {
+  using C = SmallTile;
+  static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
+  SHARQ_GEMM_LDS(C, true)
+  const GroupedTile g = grouped_tile<C>(seg, E, a_rows);
+  if (g.e < 0) return;
+  const int64_t h0 = (int64_t)blockIdx.x * 128;
+  select_expert(op, g.e, w_codes_all, w_scales_all);
+  v16f acc[C::WM][C::WN];
+  zero_acc<C>(acc);
+  mainloop_ring<C>(op, g.tr, TileCols{h0, out.I}, lds, acc, 0, op.nsteps);
+  silu_prepare_epilogue<N, M>(acc, lds, g.tr, h0, out);
 }
 
 Operands make_operands(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
@@ -973,6 +1015,27 @@ hipError_t launch_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb
     if (two) SHARQ_FUSED(SmallTile, 8, 16); else SHARQ_FUSED(DeepTile, 8, 16);
   }
 #undef SHARQ_FUSED
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                                              const uint8_t* res_codes, const uint8_t* res_scales,
+                                              const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,
+                                              const uint8_t* w_codes, const uint8_t* w_scales, int64_t P, int64_t I,
+                                              int64_t K, int64_t a_rows_total, int n, int m, uint16_t* h,
+                                              uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
+                                              uint8_t* h_res_scales, uint8_t* h_mask, hipStream_t stream) {
+  const Operands op =
+      make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, a_rows_total, 2 * I, K);
+  const HOutputs out{h, h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, P, I};
+  const int64_t tiles_m_bound = (P + SmallTile::BM - 1) / SmallTile::BM + E;
+  const dim3 grid((unsigned)(I / 128), (unsigned)tiles_m_bound);
+  if (n == 2 && m == 4)
+    hipLaunchKernelGGL((linear_grouped_silu_prepare_kernel<2, 4>), grid, dim3(kThreads), 0, stream, op, a_rows,
+                       seg_offsets, E, w_codes, w_scales, out);
+  else
+    hipLaunchKernelGGL((linear_grouped_silu_prepare_kernel<8, 16>), grid, dim3(kThreads), 0, stream, op, a_rows,
+                       seg_offsets, E, w_codes, w_scales, out);
   return hipGetLastError();
 }
 

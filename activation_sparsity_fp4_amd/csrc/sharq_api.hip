@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -165,6 +165,40 @@ int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales,
   return hip_status(sharq::launch_linear_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales,
                                                       T, I, K, n, m, h, h_bb_codes, h_bb_scales, h_res_codes,
                                                       h_res_scales, h_mask, stream));
+}
+
+int sharq_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                                      const uint8_t* res_scales, int64_t T_src, const int32_t* a_rows,
+                                      const int32_t* seg_offsets, int32_t E, const uint8_t* w_codes,
+                                      const uint8_t* w_scales, int64_t P, int64_t I, int64_t K, int n, int m,
+                                      uint16_t* h, uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
+                                      uint8_t* h_res_scales, uint8_t* h_mask, hipStream_t stream) {
+  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
+  if (E < 1 || P < 0 || I <= 0 || K <= 0 || K % 32 != 0 || I % 32 != 0 || T_src < 0) return SHARQ_EINVAL;
+  if (!a_rows && T_src < P) return SHARQ_EINVAL;
+  if (T_src >= ((int64_t)1 << 31) || P >= ((int64_t)1 << 31) || I >= ((int64_t)1 << 30) ||
+      K >= ((int64_t)1 << 31) || (P + 127) / 128 + E > 65535)
+    return SHARQ_EINVAL;
+  if (P * (I / 32) >= ((int64_t)1 << 31)) return SHARQ_EINVAL;  // 32-bit block index of the h blocks
+  if (I % 128 != 0 || K % 128 != 0) return SHARQ_ENOTIMPL;     // whole 128-column h tiles, ring path only
+  if (T_src * (K / 2) >= ((int64_t)1 << 31) || 2 * I * (K / 2) >= ((int64_t)1 << 31)) return SHARQ_ENOTIMPL;
+  const bool prep = h_bb_codes || h_bb_scales || h_res_codes || h_res_scales;
+  if (prep && !(h_bb_codes && h_bb_scales && h_res_codes && h_res_scales)) return SHARQ_EINVAL;
+  if (!prep && h_mask) return SHARQ_EINVAL;
+  if (!prep && !h) return SHARQ_EINVAL;
+  if (P == 0) return SHARQ_OK;
+  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !seg_offsets || !w_codes || !w_scales)
+    return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
+      !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(seg_offsets) || (a_rows && !aligned16(a_rows)) ||
+      (h && !aligned16(h)) ||
+      (prep && (!aligned16(h_bb_codes) || !aligned16(h_bb_scales) || !aligned16(h_res_codes) ||
+                !aligned16(h_res_scales))) ||
+      (h_mask && !aligned16(h_mask)))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_linear_grouped_silu_prepare(
+      bb_codes, bb_scales, res_codes, res_scales, a_rows, seg_offsets, E, w_codes, w_scales, P, I, K, T_src, n, m, h,
+      h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, stream));
 }
 
 int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {

@@ -195,23 +195,38 @@ def build_workload(name, torch, sq, unfused=False):
         seg = torch.from_numpy(wl["seg_offsets"]).cuda()
         rows = torch.from_numpy(wl["a_rows"]).cuda()
         buf = {"p1": sq.prepare(x, None, 2, 4)}
-        buf["gu"] = sq.linear_grouped(buf["p1"], w_gu, seg, rows)
-        buf["h"] = sq.silu_mul(buf["gu"])
-        buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
-        buf["y"] = sq.linear_grouped(buf["p2"], w_dn, seg, None)
         fa1, fe1 = gemm_flops(P, 2 * I, H)
         fa2, fe2 = gemm_flops(P, H, I)
+        gu_in_bytes = 2 * P * H * 17 / 32 + E * 2 * I * H * 17 / 32  # gathered A of both paths + all experts' W
+        if unfused:
+            buf["gu"] = sq.linear_grouped(buf["p1"], w_gu, seg, rows)
+            buf["h"] = sq.silu_mul(buf["gu"])
+            buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
+            middle = [
+                Stage("grouped_gate_up", lambda: sq.linear_grouped(buf["p1"], w_gu, seg, rows, out=buf["gu"]), "hbm",
+                      gu_in_bytes + 4 * P * 2 * I, fa1, fe1),
+                Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(P, I)),
+                Stage("prepare_pairs", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
+                      prepare_bytes(P, I)),
+            ]
+        else:
+            buf["p2"], _ = sq.linear_grouped_silu_prepare(buf["p1"], w_gu, seg, rows, 2, 4)
+            middle = [
+                Stage("grouped_gate_up_silu_prepare",
+                      lambda: sq.linear_grouped_silu_prepare(buf["p1"], w_gu, seg, rows, 2, 4, out=buf["p2"]), "hbm",
+                      gu_in_bytes + prepare_bytes(P, I) - 2 * P * I, fa1, fe1),
+            ]
+        buf["y"] = sq.linear_grouped(buf["p2"], w_dn, seg, None)
         stages = [
-            Stage("prepare_tokens", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(tokens, H)),
-            Stage("grouped_gate_up", lambda: sq.linear_grouped(buf["p1"], w_gu, seg, rows, out=buf["gu"]), "hbm",
-                  2 * P * H * 17 / 32 + E * 2 * I * H * 17 / 32 + 4 * P * 2 * I, fa1, fe1),
-            Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(P, I)),
-            Stage("prepare_pairs", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm", prepare_bytes(P, I)),
+            Stage("prepare_tokens", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(tokens, H))
+        ] + middle + [
             Stage("grouped_down", lambda: sq.linear_grouped(buf["p2"], w_dn, seg, None, out=buf["y"]), "hbm",
                   2 * P * I * 17 / 32 + E * H * I * 17 / 32 + 4 * P * H, fa2, fe2),
         ]
         cfg = {"workload": "Qwen3-30B-A3B MoE expert layer, 4096 tokens, top-8 of 128, 2:4, MXFP4",
-               "tokens": tokens, "pairs": P, "experts": E, "hidden": H, "intermediate": I, "nm": "2:4"}
+               "tokens": tokens, "pairs": P, "experts": E, "hidden": H, "intermediate": I, "nm": "2:4",
+               "gate_up": "unfused (linear_grouped, silu_mul, prepare)" if unfused
+               else "fused (linear_grouped_silu_prepare)"}
         return stages, tokens, cfg, None
 
     raise SystemExit(f"unknown workload {name}; choose from {WORKLOADS}")
@@ -282,6 +297,28 @@ def cpu_baseline(oracle_sample, tokens_full, budget_s=20.0):
                       f"(weights quantised inside the timed call), {dt:.2f} s; BLAS {blas_name} with {threads} threads"}
 
 
+def cold_cache_times(stages, steps, torch):
+    """Per-stage times with the caches cold: before each step a 1 GiB write
+    evicts L2 and the 256 MB MALL, so every stage reads its inputs from HBM
+    (the timed loop runs steps back to back, where weights and activations
+    that fit stay cached between steps). Returns (ms per step, {stage: us})."""
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    n = len(stages)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    for k in range(steps):
+        scratch.fill_(float(k))
+        events[k][0].record()
+        for i, s in enumerate(stages):
+            s.fn()
+            events[k][i + 1].record()
+    torch.cuda.synchronize()
+    step_ms = float(np.mean([events[k][0].elapsed_time(events[k][n]) for k in range(steps)]))
+    us = {s.name: round(1e3 * float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)])), 2)
+          for i, s in enumerate(stages)}
+    del scratch
+    return step_ms, us
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +330,7 @@ def main():
                     help="llama8b_mlp: run gate|up, silu_mul and prepare(h) as three kernels")
     ap.add_argument("--profile-stage", default=None,
                     help="run only this stage in warmup and timing (per-kernel profiling; not a step)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache stage timing")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device copy of this many bytes (reference for counter scaling)")
     args = ap.parse_args()
@@ -374,6 +412,11 @@ def main():
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "mxfp4", "data": "synthetic", "config": cfg, "roofline": roof, "stages": breakdown,
     }
+    if not args.profile_stage and not args.no_cold:
+        cold_ms, cold_us = cold_cache_times(stages, args.steps, torch)
+        line["cold_cache"] = {"ms_per_step": round(cold_ms, 4), "tokens_per_s": round(tokens / (cold_ms * 1e-3), 1),
+                              "stages_us": cold_us,
+                              "note": "L2 and MALL evicted by a 1 GiB write before each step; not the timed region"}
     if args.profile_stage:
         line["profile_stage"] = args.profile_stage
         line["note"] = "only this stage was run; value and ms_per_step are not a full step"

@@ -225,6 +225,33 @@ SHARQ_API int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* 
                               hipStream_t stream);
 
 /*
+ * sharq_linear_grouped_silu_prepare -- the fused gate|up projection of
+ * sharq_linear_silu_prepare per expert segment, with the segments, the row
+ * gather and the per-expert weights of sharq_linear_grouped (mixture-of-
+ * experts layers: SharQ page, Abstract). Output row p is sorted pair p.
+ *  bb_codes .. res_scales, T_src, a_rows, seg_offsets, E: as for
+ *              sharq_linear_grouped;
+ *  w_codes u8 [E][G][2I][64], w_scales u8 [E][G][2I][4]: each expert's
+ *              fused weight (gate rows 0 .. I-1, up rows I .. 2I-1);
+ *  h           bf16 [P][I] or NULL;
+ *  h_bb_codes, h_res_codes u8 [I/128][P][64], h_bb_scales, h_res_scales
+ *              u8 [I/128][P][4], h_mask u8 [P][I/8] (or NULL): prepare(h)
+ *              with pattern n:m, or all four NULL (then h must be given).
+ * Outputs are bit-identical to sharq_linear_grouped + sharq_silu_mul +
+ * sharq_prepare. Requires I % 128 == 0 and K % 128 == 0 (SHARQ_ENOTIMPL
+ * otherwise), T_src * K / 2 < 2^31 and I * K < 2^31 (SHARQ_ENOTIMPL).
+ */
+SHARQ_API int sharq_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                              const uint8_t* res_codes, const uint8_t* res_scales,
+                              int64_t T_src, const int32_t* a_rows,
+                              const int32_t* seg_offsets, int32_t E,
+                              const uint8_t* w_codes, const uint8_t* w_scales,
+                              int64_t P, int64_t I, int64_t K, int n, int m,
+                              uint16_t* h, uint8_t* h_bb_codes, uint8_t* h_bb_scales,
+                              uint8_t* h_res_codes, uint8_t* h_res_scales, uint8_t* h_mask,
+                              hipStream_t stream);
+
+/*
  * sharq_silu_mul -- glue between a fused gate|up projection and the down
  * projection (not part of the method): h[t][i] = bf16(silu(g) * u) with
  * g = gu[t][i], u = gu[t][I + i], silu(g) = g / (1 + exp(-g)), fp32 math,

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 2
+    assert _lib.call("sharq_abi_version") == 3
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
@@ -195,3 +195,30 @@ def test_prepare_rms_validation():
     assert prep_rms(rms=G + 4) == _lib.SHARQ_EALIGN
     assert prep_rms(T=1, K=131104, ldx=131104) == _lib.SHARQ_ENOTIMPL  # more than 4096 blocks
     assert prep_rms(T=0, K=131072, ldx=131072) == _lib.SHARQ_OK
+
+
+def gfused(P=4, I=128, K=128, n=2, m=4, h=G, hbc=A + 0x100000, hbs=B + 0x100000, hrc=C + 0x100000,
+           hrs=D + 0x100000, hmask=0, E=2, T_src=8, a_rows=0, seg=A + 0x200000, **kw):
+    args = dict(bc=A, bs=B, rc=C, rs=D, wc=E_, ws=F)
+    args.update(kw)
+    return _lib.call("sharq_linear_grouped_silu_prepare", args["bc"], args["bs"], args["rc"], args["rs"], T_src,
+                     a_rows, seg, E, args["wc"], args["ws"], P, I, K, n, m, h, hbc, hbs, hrc, hrs, hmask, 0)
+
+
+def test_linear_grouped_silu_prepare_validation():
+    assert gfused(P=0) == _lib.SHARQ_OK
+    assert gfused(P=0, h=0) == _lib.SHARQ_OK
+    assert gfused(hbc=0, hbs=0, hrc=0, hrs=0, h=0) == _lib.SHARQ_EINVAL   # nothing to write
+    assert gfused(hrs=0) == _lib.SHARQ_EINVAL                           # prepared output half given
+    assert gfused(hbc=0, hbs=0, hrc=0, hrs=0, hmask=A) == _lib.SHARQ_EINVAL
+    assert gfused(n=4, m=8) == _lib.SHARQ_EUNSUPPORTED
+    assert gfused(E=0) == _lib.SHARQ_EINVAL
+    assert gfused(seg=0) == _lib.SHARQ_EINVAL
+    assert gfused(T_src=2) == _lib.SHARQ_EINVAL                         # identity rows need T_src >= P
+    assert gfused(K=96) == _lib.SHARQ_ENOTIMPL
+    assert gfused(I=96) == _lib.SHARQ_ENOTIMPL
+    assert gfused(I=100) == _lib.SHARQ_EINVAL
+    assert gfused(P=1 << 24, E=1, T_src=1 << 24) == _lib.SHARQ_EINVAL    # grid bound
+    assert gfused(a_rows=A + 4) == _lib.SHARQ_EALIGN
+    assert gfused(h=G + 2) == _lib.SHARQ_EALIGN
+    assert gfused(T_src=1 << 20, K=1 << 12, P=8) == _lib.SHARQ_ENOTIMPL  # activation codes past 32-bit offsets

@@ -18,11 +18,14 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 //   g <  0: ((g * u) * h) * h / (1 + h^2)  (= g u e^g / (1 + e^g))
 // The negative branch multiplies by the two half-exponentials one at a time so
 // results down to the fp32 normal range survive even when e^g alone is subnormal.
+// 1 / den (den in [1, 2]) is the hardware reciprocal (1 ulp): with the fast
+// exponential the fp32 result is a few ulp from silu(g) * u, far inside the
+// bf16 rounding that follows.
 __device__ __forceinline__ float silu_times(float g, float u) {
   const float h = __expf(-0.5f * fabsf(g));
-  const float den = 1.0f + h * h;
+  const float r = __builtin_amdgcn_rcpf(1.0f + h * h);
   const float gu = g * u;
-  return g >= 0.0f ? gu / den : ((gu * h) * h) / den;
+  return (g >= 0.0f ? gu : (gu * h) * h) * r;
 }
 
 }  // namespace sharq

@@ -36,17 +36,20 @@ struct BlockOfLane {
   bool row_ok, block_ok;
 };
 
-__device__ __forceinline__ BlockOfLane block_of_lane(uint32_t stages, uint32_t blocks_per_row, uint32_t rows) {
-  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t wave = gid >> 6, lane = gid & 63;
-  const uint32_t band = wave / stages;
-  const uint32_t g = wave - band * stages;
+__device__ __forceinline__ BlockOfLane block_of_item(uint32_t item, uint32_t lane, uint32_t stages,
+                                                     uint32_t blocks_per_row, uint32_t rows) {
+  const uint32_t band = item / stages;
+  const uint32_t g = item - band * stages;
   BlockOfLane r;
   r.t = band * 16 + (lane >> 2);
   r.b = g * 4 + (lane & 3);
   r.row_ok = r.t < rows;
   r.block_ok = r.row_ok && r.b < blocks_per_row;
   return r;
+}
+__device__ __forceinline__ BlockOfLane block_of_lane(uint32_t stages, uint32_t blocks_per_row, uint32_t rows) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  return block_of_item(gid >> 6, gid & 63, stages, blocks_per_row, rows);
 }
 
 // bf16 bits of a float32 value, rounded to nearest, ties to even (finite).
@@ -73,27 +76,27 @@ __device__ __forceinline__ void widen_block(const uint4 (&raw)[4], float (&xv)[3
   }
 }
 
-// x' = x * gamma on one block, then selection, quantisation and the stores.
-template <int N, int M, bool kGamma>
-__device__ __forceinline__ void prepare_store(float (&xv)[32], const uint16_t* __restrict__ gamma, uint32_t t,
-                                              uint32_t b, uint32_t blocks_per_row, uint32_t rows,
+__device__ __forceinline__ void times_gamma(float (&xv)[32], const uint4 (&graw)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {graw[i].x, graw[i].y, graw[i].z, graw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xv[8 * i + 2 * j] *= bf16_lo(w[j]);
+      xv[8 * i + 2 * j + 1] *= bf16_hi(w[j]);
+    }
+  }
+}
+
+// Selection, quantisation and the stores of one block of x'. kLowBits: x'
+// may carry more than bf16's 8 significant bits (a product with gamma).
+template <int N, int M, bool kLowBits>
+__device__ __forceinline__ void prepare_store(const float (&xv)[32], uint32_t t, uint32_t b,
+                                              uint32_t blocks_per_row, uint32_t rows,
                                               uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_scales,
                                               uint8_t* __restrict__ res_codes, uint8_t* __restrict__ res_scales,
                                               uint8_t* __restrict__ mask_out) {
-  if constexpr (kGamma) {
-    uint4 graw[4];
-    load_block(gamma + (int64_t)b * kBlock, graw);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w[4] = {graw[i].x, graw[i].y, graw[i].z, graw[i].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xv[8 * i + 2 * j] *= bf16_lo(w[j]);
-        xv[8 * i + 2 * j + 1] *= bf16_hi(w[j]);
-      }
-    }
-  }
-  const PreparedBlock pb = prepare_block<N, M, kGamma>(xv);
+  const PreparedBlock pb = prepare_block<N, M, kLowBits>(xv);
   *reinterpret_cast<uint4*>(bb_codes + code_offset(t, b, rows)) = pb.c_bb;
   *reinterpret_cast<uint4*>(res_codes + code_offset(t, b, rows)) = pb.c_rs;
   bb_scales[scale_index(t, b, rows)] = (uint8_t)pb.e_bb;
@@ -111,25 +114,60 @@ __device__ __forceinline__ void zero_block(uint32_t t, uint32_t b, uint32_t rows
 }
 
 // The whole operator without the norm: x' = x (times gamma when given).
+// A work item is one wave's share of block_of_item: a 16-row band times one
+// 128-entry stage. The grid holds about as many waves as the chip keeps
+// resident, and wave w walks items w, w + W, w + 2W, ... (W waves in all),
+// issuing the loads of its next item before coding the current one, so the
+// HBM reads of one item overlap the VALU work of the one before (a wave per
+// item would read, compute and store in lock step with every other wave).
 template <int N, int M, bool kGamma>
 __global__ __launch_bounds__(256) void prepare_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ gamma,
-    uint32_t blocks_per_row, uint32_t stages, uint32_t rows,
+    uint32_t blocks_per_row, uint32_t stages, uint32_t rows, uint32_t items,
     uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_scales,
     uint8_t* __restrict__ res_codes, uint8_t* __restrict__ res_scales,
     uint8_t* __restrict__ mask_out) {
-  const BlockOfLane lb = block_of_lane(stages, blocks_per_row, rows);
-  if (!lb.block_ok) {
-    // the unused blocks of a last, partial stage are zero
-    if (lb.row_ok) zero_block(lb.t, lb.b, rows, bb_codes, bb_scales, res_codes, res_scales);
-    return;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t nwaves = (gridDim.x * blockDim.x) >> 6;
+  uint32_t item = __builtin_amdgcn_readfirstlane((blockIdx.x * blockDim.x + threadIdx.x) >> 6);  // wave-uniform
+  if (item >= items) return;  // whole waves
+  // Loads are unconditional (a lane without a block reads block 0 of row 0,
+  // the last item reads itself again) so that no branch hides from the
+  // compiler how many loads are in flight: it then waits for exactly the
+  // current item's loads, never for the next item's.
+  auto load = [&](const BlockOfLane& lb, uint4 (&raw)[4], uint4 (&graw)[4]) {
+    const int64_t t = lb.block_ok ? lb.t : 0, b = lb.block_ok ? lb.b : 0;
+    load_block(x + t * ldx + b * kBlock, raw);
+    if constexpr (kGamma) load_block(gamma + b * kBlock, graw);
+  };
+  // One step: issue the next item's loads into (nraw, ngraw), code the
+  // current item from (raw, graw). Returns false after the last item. The
+  // loop below alternates the two register sets, so no copy of an in-flight
+  // load's destination forces a wait.
+  auto step = [&](BlockOfLane& lb, const uint4 (&raw)[4], const uint4 (&graw)[4], uint4 (&nraw)[4],
+                  uint4 (&ngraw)[4]) {
+    const uint32_t next = item + nwaves;
+    const bool more = next < items;  // wave-uniform
+    const BlockOfLane nb = block_of_item(more ? next : item, lane, stages, blocks_per_row, rows);
+    load(nb, nraw, ngraw);
+    if (lb.block_ok) {
+      float xv[32];
+      widen_block(raw, xv);
+      if constexpr (kGamma) times_gamma(xv, graw);
+      prepare_store<N, M, kGamma>(xv, lb.t, lb.b, blocks_per_row, rows, bb_codes, bb_scales, res_codes,
+                                  res_scales, mask_out);
+    } else if (lb.row_ok) {
+      zero_block(lb.t, lb.b, rows, bb_codes, bb_scales, res_codes, res_scales);  // partial last stage
+    }
+    item = next;
+    lb = nb;
+    return more;
+  };
+  BlockOfLane lb = block_of_item(item, lane, stages, blocks_per_row, rows);
+  uint4 raw0[4], graw0[4], raw1[4], graw1[4];
+  load(lb, raw0, graw0);
+  while (step(lb, raw0, graw0, raw1, graw1) && step(lb, raw1, graw1, raw0, graw0)) {
   }
-  uint4 raw[4];
-  load_block(x + (int64_t)lb.t * ldx + (int64_t)lb.b * kBlock, raw);
-  float xv[32];
-  widen_block(raw, xv);
-  prepare_store<N, M, kGamma>(xv, gamma, lb.t, lb.b, blocks_per_row, rows, bb_codes, bb_scales, res_codes,
-                              res_scales, mask_out);
 }
 
 // Full RMSNorm absorption (page "SharQ: ...", Abstract: the fused prepare
@@ -264,7 +302,12 @@ __global__ __launch_bounds__(256) void prepare_rms_kernel(
     widen_block(raw, xv);
 #pragma unroll
     for (int k = 0; k < 32; ++k) xv[k] = __uint_as_float(f32_to_bf16_rne(xv[k] * r) << 16);
-    prepare_store<N, M, kGamma>(xv, gamma, t, b, nb, rows, bb_codes, bb_scales, res_codes, res_scales, mask_out);
+    if constexpr (kGamma) {
+      uint4 graw[4];
+      load_block(gamma + (int64_t)b * kBlock, graw);
+      times_gamma(xv, graw);
+    }
+    prepare_store<N, M, kGamma>(xv, t, b, nb, rows, bb_codes, bb_scales, res_codes, res_scales, mask_out);
   };
 #pragma unroll
   for (int it = 0; it < kRmsHold; ++it) {
@@ -317,6 +360,33 @@ static inline uint64_t lanes_for(int64_t T, int64_t K) {
   return bands * stages * 64;
 }
 
+// Compute units of the current device (queried once per device).
+static int cu_count() {
+  static int cache[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Waves of a 256-thread kernel the current device keeps resident at once
+// (occupancy per CU times CUs), cached per device in `cache`.
+static uint64_t resident_waves(const void* kernel, int (&cache)[64]) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 256, 0) != hipSuccess || blocks <= 0)
+      blocks = 2;
+    cache[dev] = blocks;
+  }
+  return (uint64_t)cache[dev] * 4 * (uint64_t)cu_count();
+}
+
 hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma,
                           float rms_eps, float* rms_scale, int n, int m, uint8_t* bb_codes, uint8_t* bb_scales,
                           uint8_t* res_codes, uint8_t* res_scales, uint8_t* mask, hipStream_t stream) {
@@ -335,13 +405,21 @@ hipError_t launch_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, 
   }
   const uint32_t bpr = (uint32_t)(K / kBlock);
   const uint32_t stages = (uint32_t)((K + 127) / 128);
-  const uint64_t lanes = lanes_for(T, K);
-  // small problems: one wave per workgroup so that more CUs take part
-  const unsigned threads = lanes >= (1u << 18) ? 256 : 64;
-  const dim3 grid((unsigned)((lanes + threads - 1) / threads)), block(threads);
-#define SHARQ_PREP(NN, MM, GG)                                                                                \
-  hipLaunchKernelGGL((prepare_kernel<NN, MM, GG>), grid, block, 0, stream, x, ldx, gamma, bpr, stages, (uint32_t)T, \
-                     bb_codes, bb_scales, res_codes, res_scales, mask)
+  const uint64_t items = lanes_for(T, K) / 64;
+  // Waves in the grid: at most what the chip keeps resident at this
+  // variant's register use, each walking the same number of items; small
+  // grids take one wave per workgroup so that more CUs take part.
+#define SHARQ_PREP(NN, MM, GG)                                                                                    \
+  do {                                                                                                            \
+    static int resident[64] = {};                                                                                 \
+    const uint64_t cap = resident_waves(reinterpret_cast<const void*>(&prepare_kernel<NN, MM, GG>), resident);    \
+    const uint64_t per_wave = (items + cap - 1) / cap;                                                            \
+    const uint64_t waves = (items + per_wave - 1) / per_wave;                                                     \
+    const unsigned threads = waves >= 4 * (uint64_t)cu_count() ? 256 : 64;                                        \
+    hipLaunchKernelGGL((prepare_kernel<NN, MM, GG>), dim3((unsigned)((waves * 64 + threads - 1) / threads)),      \
+                       dim3(threads), 0, stream, x, ldx, gamma, bpr, stages, (uint32_t)T, (uint32_t)items, bb_codes, \
+                       bb_scales, res_codes, res_scales, mask);                                                   \
+  } while (0)
   if (n == 2 && m == 4) {
     if (gamma) SHARQ_PREP(2, 4, true); else SHARQ_PREP(2, 4, false);
   } else {

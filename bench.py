@@ -297,23 +297,45 @@ def cpu_baseline(oracle_sample, tokens_full, budget_s=20.0):
                       f"(weights quantised inside the timed call), {dt:.2f} s; BLAS {blas_name} with {threads} threads"}
 
 
+def copy_rate(torch, n_bytes=1 << 30, reps=10):
+    """Achieved HBM GB/s of a plain device-to-device copy (read + write bytes
+    over time, median of reps): the practical ceiling of a mixed read/write
+    stream, reported beside the 8 TB/s datasheet peak."""
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    del src, dst
+    return round(2 * n_bytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+
+
 def cold_cache_times(stages, steps, torch):
-    """Per-stage times with the caches cold: before each step a 1 GiB write
-    evicts L2 and the 256 MB MALL, so every stage reads its inputs from HBM
-    (the timed loop runs steps back to back, where weights and activations
-    that fit stay cached between steps). Returns (ms per step, {stage: us})."""
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    """Per-stage times with the caches cold: before each step a read of a
+    1 GiB buffer evicts L2 and the 256 MB MALL, so every stage reads its
+    inputs from HBM (the timed loop runs steps back to back, where weights and
+    activations that fit stay cached between steps). The sweep reads rather
+    than writes: a write would leave the caches full of dirty lines whose
+    write-back would then be charged to the first stages. Returns (ms per
+    step, {stage: median us})."""
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     n = len(stages)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
     for k in range(steps):
-        scratch.fill_(float(k))
+        scratch.amax()
         events[k][0].record()
         for i, s in enumerate(stages):
             s.fn()
             events[k][i + 1].record()
     torch.cuda.synchronize()
-    step_ms = float(np.mean([events[k][0].elapsed_time(events[k][n]) for k in range(steps)]))
-    us = {s.name: round(1e3 * float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)])), 2)
+    step_ms = float(np.median([events[k][0].elapsed_time(events[k][n]) for k in range(steps)]))
+    us = {s.name: round(1e3 * float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)])), 2)
           for i, s in enumerate(stages)}
     del scratch
     return step_ms, us
@@ -322,8 +344,8 @@ def cold_cache_times(stages, steps, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_mlp", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused", action="store_true",
@@ -375,7 +397,8 @@ def main():
     wall = time.perf_counter() - t0
 
     ms_per_step = 1e3 * wall / args.steps
-    stage_ms = [float(np.mean([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
+    # per-stage medians over the timed steps
+    stage_ms = [float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
                 for i in range(n)]
     breakdown = {}
     for s, ms in zip(stages, stage_ms):
@@ -413,10 +436,11 @@ def main():
         "dtype": "mxfp4", "data": "synthetic", "config": cfg, "roofline": roof, "stages": breakdown,
     }
     if not args.profile_stage and not args.no_cold:
+        line["hbm_copy_GBps"] = copy_rate(torch)
         cold_ms, cold_us = cold_cache_times(stages, args.steps, torch)
         line["cold_cache"] = {"ms_per_step": round(cold_ms, 4), "tokens_per_s": round(tokens / (cold_ms * 1e-3), 1),
                               "stages_us": cold_us,
-                              "note": "L2 and MALL evicted by a 1 GiB write before each step; not the timed region"}
+                              "note": "L2 and MALL evicted by a 1 GiB read before each step; medians; not the timed region"}
     if args.profile_stage:
         line["profile_stage"] = args.profile_stage
         line["note"] = "only this stage was run; value and ms_per_step are not a full step"

@@ -245,11 +245,13 @@ def linear_grouped(prep: Prepared, w: MXFP4, seg_offsets, a_rows=None, out=None)
 
 
 def linear_silu_prepare(prep: Prepared, w_gu: MXFP4, n: int = 2, m: int = 4, with_h: bool = False,
-                        with_prepared: bool = True, with_mask: bool = True):
+                        with_prepared: bool = True, with_mask: bool = True, split_k: bool = True):
     """Fused gate|up projection: Y = two-path GEMM of prep against w_gu (rows:
     I gate rows, then I up rows), h = bf16(silu(Y[:, :I]) * Y[:, I:]), then
     prepare(h, n, m). Returns (Prepared of h or None, h or None); the results
-    equal linear -> silu_mul -> prepare bit for bit."""
+    equal linear(split_k) -> silu_mul -> prepare bit for bit. With split_k,
+    problems with too few tiles to fill the GPU split K as linear does
+    (sharq_linear_silu_prepare_ws over the cached workspace)."""
     torch = _torch()
     _check_prepared(prep)
     _need(w_gu.codes, torch.uint8, "w_gu.codes", 3)
@@ -269,27 +271,35 @@ def linear_silu_prepare(prep: Prepared, w_gu: MXFP4, n: int = 2, m: int = 4, wit
         hp = Prepared(torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
                       torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
                       torch.empty((T, I // 8), **kw) if with_mask else None, I)
-    _fused_call(prep, w_gu, T, I, K, n, m, h, hp)
+    _fused_call(prep, w_gu, T, I, K, n, m, h, hp, split_k)
     return hp, h
 
 
-def linear_silu_prepare_into(prep: Prepared, w_gu: MXFP4, out: Prepared, n: int = 2, m: int = 4) -> Prepared:
+def linear_silu_prepare_into(prep: Prepared, w_gu: MXFP4, out: Prepared, n: int = 2, m: int = 4,
+                             split_k: bool = True) -> Prepared:
     """linear_silu_prepare writing prepare(h) into preallocated `out` (no h)."""
     _check_prepared(prep)
     _check_prepared(out)
     T, K, I = prep.bb_codes.shape[1], prep.K, out.K
     if w_gu.K != K or tuple(w_gu.codes.shape) != (stages(K), 2 * I, 64) or out.bb_codes.shape[1] != T:
         raise ValueError("shapes of prep, w_gu and out do not match")
-    _fused_call(prep, w_gu, T, I, K, n, m, None, out)
+    _fused_call(prep, w_gu, T, I, K, n, m, None, out, split_k)
     return out
 
 
-def _fused_call(prep, w_gu, T, I, K, n, m, h, hp):
-    st = _lib.call("sharq_linear_silu_prepare", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
-                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), w_gu.codes.data_ptr(),
-                   w_gu.scales.data_ptr(), T, I, K, n, m, _ptr(h),
-                   _ptr(hp and hp.bb_codes), _ptr(hp and hp.bb_scales), _ptr(hp and hp.res_codes),
-                   _ptr(hp and hp.res_scales), _ptr(hp and hp.mask), _stream(prep.bb_codes.device))
+def _fused_call(prep, w_gu, T, I, K, n, m, h, hp, split_k):
+    dev = prep.bb_codes.device
+    args = (prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(), prep.res_codes.data_ptr(),
+            prep.res_scales.data_ptr(), w_gu.codes.data_ptr(), w_gu.scales.data_ptr(), T, I, K, n, m, _ptr(h),
+            _ptr(hp and hp.bb_codes), _ptr(hp and hp.bb_scales), _ptr(hp and hp.res_codes),
+            _ptr(hp and hp.res_scales), _ptr(hp and hp.mask))
+    nbytes = _lib.call("sharq_linear_workspace_bytes", T, 2 * I, K) if split_k else 0
+    if nbytes > 0:
+        ws = _workspace(dev, nbytes)
+        st = _lib.call("sharq_linear_silu_prepare_ws", *args, ws.data_ptr(), ws.numel(), _stream(dev))
+        _lib.check("sharq_linear_silu_prepare_ws", st)
+        return
+    st = _lib.call("sharq_linear_silu_prepare", *args, _stream(dev))
     _lib.check("sharq_linear_silu_prepare", st)
 
 

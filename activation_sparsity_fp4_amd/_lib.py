@@ -38,6 +38,8 @@ SIGNATURES = {
                                     _P]),
     "sharq_linear_silu_prepare": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P,
                                          _P, _P, _P]),
+    "sharq_linear_silu_prepare_ws": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P,
+                                            _P, _P, _P, _I64, _P]),
     "sharq_linear_grouped_silu_prepare": (_INT, [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _I64, _I64,
                                                  _I64, _INT, _INT, _P, _P, _P, _P, _P, _P, _P]),
     "sharq_silu_mul": (_INT, [_P, _I64, _I64, _P, _P]),

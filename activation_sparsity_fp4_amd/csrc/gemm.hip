@@ -923,6 +923,70 @@ __global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_k
   silu_prepare_epilogue<N, M>(acc, lds, tr, h0, out);
 }
 
+// Split-K form of the fused gate|up epilogue, for problems with too few
+// tiles to fill the GPU (decode-sized T). linear_split_kernel has stored the
+// partials [S][T][2I] of the plain gate|up GEMM; here lane (t, b) owns the
+// 32-entry h block b of row t (a wave: a 16-row band of one 128-entry stage,
+// as in the prepare kernel), sums the S partials of its 32 gate and 32 up
+// outputs in split order 0, 1, ..., S-1 (as split_reduce_kernel), forms
+// h = bf16(silu(g) * u) (as the SiLU kernel) and codes the block with the
+// per-block prepare code. The results equal linear (split-K) -> silu_mul ->
+// prepare bit for bit, with neither the fp32 gate|up output nor h in HBM.
+template <int N, int M>
+__global__ __launch_bounds__(256) void split_reduce_silu_prepare_kernel(const float* __restrict__ partials, int S,
+                                                                        HOutputs out) {
+  const uint32_t gid = blockIdx.x * 256 + threadIdx.x;
+  const uint32_t item = gid >> 6, lane = gid & 63;
+  const uint32_t stages = (uint32_t)(out.I / 128);
+  const uint32_t band = item / stages, g = item - band * stages;
+  const int64_t t = (int64_t)band * 16 + (lane >> 2);
+  const uint32_t b = g * 4 + (lane & 3);
+  if (t >= out.T) return;  // per lane: no barrier follows
+  const int64_t plane = out.T * 2 * out.I;
+  const float* gsrc = partials + t * 2 * out.I + 32 * (int64_t)b;
+  const float* usrc = gsrc + out.I;
+  float gv[32], uv[32];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4 a = reinterpret_cast<const float4*>(gsrc)[k];
+    const float4 c = reinterpret_cast<const float4*>(usrc)[k];
+    gv[4 * k] = a.x, gv[4 * k + 1] = a.y, gv[4 * k + 2] = a.z, gv[4 * k + 3] = a.w;
+    uv[4 * k] = c.x, uv[4 * k + 1] = c.y, uv[4 * k + 2] = c.z, uv[4 * k + 3] = c.w;
+  }
+  for (int q = 1; q < S; ++q) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 a = reinterpret_cast<const float4*>(gsrc + q * plane)[k];
+      const float4 c = reinterpret_cast<const float4*>(usrc + q * plane)[k];
+      gv[4 * k] += a.x, gv[4 * k + 1] += a.y, gv[4 * k + 2] += a.z, gv[4 * k + 3] += a.w;
+      uv[4 * k] += c.x, uv[4 * k + 1] += c.y, uv[4 * k + 2] += c.z, uv[4 * k + 3] += c.w;
+    }
+  }
+  float hv[32];
+  uint32_t hb[16];
+#pragma unroll
+  for (int k = 0; k < 32; k += 2) {
+    const uint32_t lo = bf16_rne_bits(silu_times(gv[k], uv[k]));
+    const uint32_t hi = bf16_rne_bits(silu_times(gv[k + 1], uv[k + 1]));
+    hb[k / 2] = lo | (hi << 16);
+    hv[k] = __uint_as_float(lo << 16);
+    hv[k + 1] = __uint_as_float(hi << 16);
+  }
+  if (out.h) {
+    uint4* dst = reinterpret_cast<uint4*>(out.h + t * out.I + 32 * (int64_t)b);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_uint4(hb[4 * q], hb[4 * q + 1], hb[4 * q + 2], hb[4 * q + 3]);
+  }
+  if (out.bb_codes) {
+    const PreparedBlock pb = prepare_block<N, M, false>(hv);
+    *reinterpret_cast<uint4*>(out.bb_codes + code_offset(t, b, out.T)) = pb.c_bb;
+    *reinterpret_cast<uint4*>(out.res_codes + code_offset(t, b, out.T)) = pb.c_rs;
+    out.bb_scales[scale_index(t, b, out.T)] = (uint8_t)pb.e_bb;
+    out.res_scales[scale_index(t, b, out.T)] = (uint8_t)pb.e_rs;
+    if (out.mask) reinterpret_cast<uint32_t*>(out.mask)[t * (out.I >> 5) + b] = pb.keep;
+  }
+}
+
 // Grouped form of the fused gate|up projection (mixture-of-experts layers):
 // the tile of linear_grouped_kernel's row walk with the fused epilogue;
 // blockIdx.x is the 128-column h tile.
@@ -1068,6 +1132,32 @@ hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scal
   else
     hipLaunchKernelGGL(linear_grouped_kernel<false>, grid, dim3(kThreads), 0, stream, op, a_rows, seg_offsets, E,
                        w_codes, w_scales, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                                         const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                                         int64_t T, int64_t I, int64_t K, int n, int m, uint16_t* h,
+                                         uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
+                                         uint8_t* h_res_scales, uint8_t* h_mask, void* workspace,
+                                         int64_t workspace_bytes, hipStream_t stream) {
+  const SplitPlan p = split_plan(T, 2 * I, K);
+  if (p.S < 2 || !workspace || workspace_bytes < p.partial_bytes)
+    return launch_linear_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, I, K, n, m, h,
+                                      h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, stream);
+  const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, 2 * I, K);
+  float* partials = static_cast<float*>(workspace);
+  hipLaunchKernelGGL((linear_split_kernel<SmallTile>), dim3(p.tiles_total * p.S), dim3(kThreads), 0, stream, op, T,
+                     p.tiles_m, p.tiles_total, p.S, partials);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const HOutputs out{h, h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, T, I};
+  const uint64_t lanes = (uint64_t)((T + 15) / 16) * (uint64_t)(I / 128) * 64;
+  const dim3 grid((unsigned)((lanes + 255) / 256));
+  if (n == 2 && m == 4)
+    hipLaunchKernelGGL((split_reduce_silu_prepare_kernel<2, 4>), grid, dim3(256), 0, stream, partials, p.S, out);
+  else
+    hipLaunchKernelGGL((split_reduce_silu_prepare_kernel<8, 16>), grid, dim3(256), 0, stream, partials, p.S, out);
   return hipGetLastError();
 }
 

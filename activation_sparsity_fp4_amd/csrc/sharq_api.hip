@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -20,6 +20,36 @@ int check_rows(int64_t T, int64_t K, int64_t ldx) {
   if (T >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
   if (T * (K / 32) >= ((int64_t)1 << 31)) return SHARQ_EINVAL;  // 32-bit block index
   if (ldx % 8 != 0) return SHARQ_EALIGN;
+  return SHARQ_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Argument checks shared by sharq_linear_silu_prepare and its split-K form.
+int check_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                       const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,
+                       int64_t I, int64_t K, int n, int m, uint16_t* h, uint8_t* h_bb_codes, uint8_t* h_bb_scales,
+                       uint8_t* h_res_codes, uint8_t* h_res_scales, uint8_t* h_mask) {
+  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
+  if (T < 0 || I <= 0 || K <= 0 || K % 32 != 0 || I % 32 != 0) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || I >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (T * (I / 32) >= ((int64_t)1 << 31)) return SHARQ_EINVAL;  // 32-bit block index of the h blocks
+  if (I % 128 != 0 || K % 128 != 0) return SHARQ_ENOTIMPL;     // whole 128-column h tiles, ring path only
+  if (T * (K / 2) >= ((int64_t)1 << 31) || 2 * I * (K / 2) >= ((int64_t)1 << 31)) return SHARQ_ENOTIMPL;
+  const bool prep = h_bb_codes || h_bb_scales || h_res_codes || h_res_scales;
+  if (prep && !(h_bb_codes && h_bb_scales && h_res_codes && h_res_scales)) return SHARQ_EINVAL;
+  if (!prep && h_mask) return SHARQ_EINVAL;
+  if (!prep && !h) return SHARQ_EINVAL;  // nothing to write
+  if (T == 0) return SHARQ_OK;
+  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !w_codes || !w_scales) return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
+      !aligned16(w_codes) || !aligned16(w_scales) || (h && !aligned16(h)) ||
+      (prep && (!aligned16(h_bb_codes) || !aligned16(h_bb_scales) || !aligned16(h_res_codes) ||
+                !aligned16(h_res_scales))) ||
+      (h_mask && !aligned16(h_mask)))
+    return SHARQ_EALIGN;
   return SHARQ_OK;
 }
 
@@ -139,32 +169,34 @@ int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales, cons
                                                  E, w_codes, w_scales, P, O, K, y, T_src, stream));
 }
 
+
 int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
                               const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,
                               int64_t I, int64_t K, int n, int m, uint16_t* h, uint8_t* h_bb_codes,
                               uint8_t* h_bb_scales, uint8_t* h_res_codes, uint8_t* h_res_scales, uint8_t* h_mask,
                               hipStream_t stream) {
-  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
-  if (T < 0 || I <= 0 || K <= 0 || K % 32 != 0 || I % 32 != 0) return SHARQ_EINVAL;
-  if (T >= ((int64_t)1 << 31) || I >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
-  if (T * (I / 32) >= ((int64_t)1 << 31)) return SHARQ_EINVAL;  // 32-bit block index of the h blocks
-  if (I % 128 != 0 || K % 128 != 0) return SHARQ_ENOTIMPL;     // whole 128-column h tiles, ring path only
-  if (T * (K / 2) >= ((int64_t)1 << 31) || 2 * I * (K / 2) >= ((int64_t)1 << 31)) return SHARQ_ENOTIMPL;
-  const bool prep = h_bb_codes || h_bb_scales || h_res_codes || h_res_scales;
-  if (prep && !(h_bb_codes && h_bb_scales && h_res_codes && h_res_scales)) return SHARQ_EINVAL;
-  if (!prep && h_mask) return SHARQ_EINVAL;
-  if (!prep && !h) return SHARQ_EINVAL;  // nothing to write
-  if (T == 0) return SHARQ_OK;
-  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !w_codes || !w_scales) return SHARQ_EINVAL;
-  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
-      !aligned16(w_codes) || !aligned16(w_scales) || (h && !aligned16(h)) ||
-      (prep && (!aligned16(h_bb_codes) || !aligned16(h_bb_scales) || !aligned16(h_res_codes) ||
-                !aligned16(h_res_scales))) ||
-      (h_mask && !aligned16(h_mask)))
-    return SHARQ_EALIGN;
+  const int rc = check_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, I, K, n, m, h,
+                                    h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask);
+  if (rc != SHARQ_OK || T == 0) return rc;
   return hip_status(sharq::launch_linear_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales,
                                                       T, I, K, n, m, h, h_bb_codes, h_bb_scales, h_res_codes,
                                                       h_res_scales, h_mask, stream));
+}
+
+int sharq_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                                 const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                                 int64_t T, int64_t I, int64_t K, int n, int m, uint16_t* h, uint8_t* h_bb_codes,
+                                 uint8_t* h_bb_scales, uint8_t* h_res_codes, uint8_t* h_res_scales, uint8_t* h_mask,
+                                 void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  const int rc = check_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, I, K, n, m, h,
+                                    h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask);
+  if (rc != SHARQ_OK || T == 0) return rc;
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace)) return SHARQ_EINVAL;
+  if (workspace && !aligned16(workspace)) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_linear_silu_prepare_ws(bb_codes, bb_scales, res_codes, res_scales, w_codes,
+                                                         w_scales, T, I, K, n, m, h, h_bb_codes, h_bb_scales,
+                                                         h_res_codes, h_res_scales, h_mask, workspace,
+                                                         workspace_bytes, stream));
 }
 
 int sharq_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,

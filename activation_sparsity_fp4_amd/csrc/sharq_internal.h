@@ -38,6 +38,13 @@ hipError_t launch_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb
                                       uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
                                       uint8_t* h_res_scales, uint8_t* h_mask, hipStream_t stream);
 
+hipError_t launch_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                                         const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                                         int64_t T, int64_t I, int64_t K, int n, int m, uint16_t* h,
+                                         uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
+                                         uint8_t* h_res_scales, uint8_t* h_mask, void* workspace,
+                                         int64_t workspace_bytes, hipStream_t stream);
+
 hipError_t launch_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales,
                                               const uint8_t* res_codes, const uint8_t* res_scales,
                                               const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,

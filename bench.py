@@ -166,22 +166,34 @@ def build_workload(name, torch, sq, unfused=False):
         w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"]))
         w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"]))
         buf = {"p1": sq.prepare(x, None, 2, 4)}
-        buf["gu"] = sq.linear(buf["p1"], w_gu)
-        buf["h"] = sq.silu_mul(buf["gu"])
-        buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
-        buf["y"] = sq.linear(buf["p2"], w_dn)
         fa1, fe1 = gemm_flops(T, 2 * I, H)
         fa2, fe2 = gemm_flops(T, H, I)
-        stages = [
-            Stage("prepare_x", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(T, H)),
-            Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "hbm", gemm_bytes(T, 2 * I, H),
-                  fa1, fe1),
-            Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
-            Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm", prepare_bytes(T, I)),
+        if unfused:
+            buf["gu"] = sq.linear(buf["p1"], w_gu)
+            buf["h"] = sq.silu_mul(buf["gu"])
+            buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
+            middle = [
+                Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "hbm",
+                      gemm_bytes(T, 2 * I, H), fa1, fe1),
+                Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
+                Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
+                      prepare_bytes(T, I)),
+            ]
+        else:
+            buf["p2"], _ = sq.linear_silu_prepare(buf["p1"], w_gu, 2, 4)
+            middle = [
+                Stage("gemm_gate_up_silu_prepare",
+                      lambda: sq.linear_silu_prepare_into(buf["p1"], w_gu, buf["p2"], 2, 4), "hbm",
+                      fused_bytes(T, I, H), fa1, fe1),
+            ]
+        buf["y"] = sq.linear(buf["p2"], w_dn)
+        stages = [Stage("prepare_x", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(T, H))
+                  ] + middle + [
             Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "hbm", gemm_bytes(T, H, I), fa2, fe2),
         ]
         cfg = {"workload": f"Llama-3.1-70B MLP decode, {T} tokens, 2:4, MXFP4", "tokens": T, "hidden": H,
-               "intermediate": I, "nm": "2:4"}
+               "intermediate": I, "nm": "2:4",
+               "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)"}
         return stages, T, cfg, None
 
     if name == "qwen3_moe":

@@ -225,6 +225,32 @@ SHARQ_API int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* 
                               hipStream_t stream);
 
 /*
+ * sharq_linear_silu_prepare_ws -- sharq_linear_silu_prepare with the split-K
+ * plan of sharq_linear_ws for problems with too few output tiles to fill the
+ * GPU (decode-sized T): the gate|up GEMM stores fp32 partials over K slices
+ * in `workspace`, and one more kernel sums them in slice order, forms h and
+ * codes prepare(h) (glue and prepare as in sharq_linear_silu_prepare; the
+ * method is the SharQ page's, Abstract and Section 1).
+ *  arguments as sharq_linear_silu_prepare, plus
+ *  workspace, workspace_bytes: caller-owned device memory of at least
+ *              sharq_linear_workspace_bytes(T, 2 I, K) bytes, 16-byte
+ *              aligned; contents need no initialisation and are overwritten.
+ *              With a smaller (or NULL) workspace, or when that function
+ *              returns 0, this is sharq_linear_silu_prepare.
+ * Outputs are bit-identical to sharq_linear_ws + sharq_silu_mul +
+ * sharq_prepare with the same workspace plan. Errors: as
+ * sharq_linear_silu_prepare; workspace_bytes < 0, or > 0 with a NULL
+ * workspace, is SHARQ_EINVAL; a misaligned workspace SHARQ_EALIGN.
+ */
+SHARQ_API int sharq_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                              const uint8_t* res_codes, const uint8_t* res_scales,
+                              const uint8_t* w_codes, const uint8_t* w_scales,
+                              int64_t T, int64_t I, int64_t K, int n, int m,
+                              uint16_t* h, uint8_t* h_bb_codes, uint8_t* h_bb_scales,
+                              uint8_t* h_res_codes, uint8_t* h_res_scales, uint8_t* h_mask,
+                              void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
  * sharq_linear_grouped_silu_prepare -- the fused gate|up projection of
  * sharq_linear_silu_prepare per expert segment, with the segments, the row
  * gather and the per-expert weights of sharq_linear_grouped (mixture-of-

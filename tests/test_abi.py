@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 3
+    assert _lib.call("sharq_abi_version") == 4
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
@@ -222,3 +222,24 @@ def test_linear_grouped_silu_prepare_validation():
     assert gfused(a_rows=A + 4) == _lib.SHARQ_EALIGN
     assert gfused(h=G + 2) == _lib.SHARQ_EALIGN
     assert gfused(T_src=1 << 20, K=1 << 12, P=8) == _lib.SHARQ_ENOTIMPL  # activation codes past 32-bit offsets
+
+
+def fused_ws(ws=A + 0x400000, nbytes=1 << 20, **kw):
+    args = dict(T=4, I=128, K=128, n=2, m=4, h=G, hbc=A + 0x100000, hbs=B + 0x100000, hrc=C + 0x100000,
+                hrs=D + 0x100000, hmask=0)
+    args.update(kw)
+    return _lib.call("sharq_linear_silu_prepare_ws", A, B, C, D, E_, F, args["T"], args["I"], args["K"], args["n"],
+                     args["m"], args["h"], args["hbc"], args["hbs"], args["hrc"], args["hrs"], args["hmask"], ws,
+                     nbytes, 0)
+
+
+def test_linear_silu_prepare_ws_validation():
+    assert fused_ws(T=0) == _lib.SHARQ_OK
+    assert fused_ws(T=0, ws=0, nbytes=0) == _lib.SHARQ_OK
+    assert fused_ws(n=4, m=8) == _lib.SHARQ_EUNSUPPORTED
+    assert fused_ws(K=96) == _lib.SHARQ_ENOTIMPL
+    assert fused_ws(hbs=0) == _lib.SHARQ_EINVAL
+    assert fused_ws(nbytes=-1) == _lib.SHARQ_EINVAL
+    assert fused_ws(ws=0, nbytes=16) == _lib.SHARQ_EINVAL
+    assert fused_ws(ws=A + 0x400004) == _lib.SHARQ_EALIGN
+    assert fused_ws(h=G + 2) == _lib.SHARQ_EALIGN

@@ -86,3 +86,42 @@ def test_fused_llama8b_gate_up_full_size(sq):
     wl = workload_llama8b_mlp()
     rows = np.unique(np.concatenate([[0, 2047], np.random.default_rng(2).choice(2048, 24, replace=False)]))
     _check_fused(sq, wl["x"], wl["gamma"], wl["w_gu"], 2, 4, rows)
+
+
+@pytest.mark.parametrize("T,I,K,n,m", [(1, 1024, 4096, 2, 4), (5, 512, 2048, 8, 16), (64, 1024, 4096, 2, 4),
+                                       (200, 512, 4096, 8, 16)])
+def test_fused_split_k_matches_split_chain(sq, T, I, K, n, m):
+    # decode-sized T: the fused entry splits K as linear does (S = 4 .. 8 here) and sums, gates and
+    # prepares in one more kernel; the chain is linear (same split plan) -> silu_mul -> prepare
+    import torch
+    from activation_sparsity_fp4_amd import _lib
+    S_bytes = _lib.call("sharq_linear_workspace_bytes", T, 2 * I, K)
+    assert S_bytes > 0, "the shape must take the split-K path"
+    print(f"fused split-K T={T} I={I} K={K} {n}:{m} workspace {S_bytes}", flush=True)
+    x, w = _inputs(T, I, K, seed=7 * T + I + K)
+    rows = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).choice(T, min(T, 16), replace=False)]))
+    _check_fused(sq, x, None, w, n, m, rows)
+
+
+def test_fused_split_k_llama70b_decode_gate_up(sq):
+    # the Llama-3.1-70B decode gate|up at T = 1 (2 x 28672 outputs, K = 8192: two K slices); weights drawn
+    # on the GPU from a fixed seed (the reference is the GPU chain, itself checked against the oracle)
+    import torch
+    print("fused split-K llama70b decode gate|up T=1", flush=True)
+    g = torch.Generator(device="cuda").manual_seed(70)
+    I, K = 28672, 8192
+    w = sq.quantize_mxfp4((torch.randn(2 * I, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16))
+    rng = np.random.default_rng(70)
+    x = bf16_round((rng.standard_normal((1, K)) * 2).astype(np.float32))
+    p1 = sq.prepare(bf16_to_gpu(x), None, 2, 4)
+    y = sq.linear(p1, w)
+    h_ref = sq.silu_mul(y)
+    p2_ref = sq.prepare(h_ref, None, 2, 4)
+    hp, h = sq.linear_silu_prepare(p1, w, 2, 4, with_h=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(h), to_np(h_ref))
+    for f in FIELDS:
+        assert np.array_equal(to_np(getattr(hp, f)), to_np(getattr(p2_ref, f))), f
+    h_np = to_np(h)
+    assert_prepare_equal(hp, prepare_ref(h_np, None, 2, 4))
+    assert_bf16_close(h_np, silu_mul_ref(to_np(y), I))

@@ -32,8 +32,8 @@
 // waits, load issue and output stores overlap the other's MFMAs (measured:
 // 15% faster on the Llama-3.1-8B gate|up shape than one workgroup per CU with
 // a ring of 4, and 10% faster than 256 x 256 tiles). Problems with fewer
-// tiles than two per CU keep one workgroup per CU and a ring of 4. General
-// path (any K % 32 == 0): 2 LDS stages filled through registers.
+// tiles than CUs take one workgroup per CU and a ring of 4. General path
+// (any K % 32 == 0): 2 LDS stages filled through registers.
 //
 // LDS rows are 64 bytes; the 16-byte chunk c of row r sits at chunk position
 // c ^ ((r >> 2) & 3), which keeps the rows read by one MFMA fragment on
@@ -1032,6 +1032,11 @@ bool ring_path_ok(int64_t rows, int64_t O, int64_t K) {
 
 // Tiles for two workgroups on each of MI355X's 256 CUs.
 constexpr int64_t kTwoPerCu = 512;
+// Problems with at least one tile per CU take the ring of 2 (which leaves LDS
+// for a second workgroup per CU); below that the ring of 4. At exactly one
+// tile per CU (the Llama-3.1-8B down projection) the ring of 2 measured 3%
+// faster than the ring of 4.
+constexpr int64_t kSmallTileMin = 256;
 
 template <class C, bool kRingPath>
 void launch_tiles(const Operands& op, int64_t T, float* y, int64_t ldy, hipStream_t stream) {
@@ -1108,7 +1113,7 @@ hipError_t launch_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, cons
   const int64_t tiles = ((T + SmallTile::BM - 1) / SmallTile::BM) * ((O + SmallTile::BN - 1) / SmallTile::BN);
   if (!ring_path_ok(T, O, K))
     launch_tiles<SmallTile, false>(op, T, y, ldy, stream);
-  else if (tiles >= kTwoPerCu)
+  else if (tiles >= kSmallTileMin)
     launch_tiles<SmallTile, true>(op, T, y, ldy, stream);
   else
     launch_tiles<DeepTile, true>(op, T, y, ldy, stream);
@@ -1170,7 +1175,7 @@ hipError_t launch_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb
   const HOutputs out{h, h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, T, I};
   const int tiles_m = (int)((T + 127) / 128);
   const int total = tiles_m * (int)(I / 128);
-  const bool two = total >= kTwoPerCu;
+  const bool two = total >= kSmallTileMin;
 #define SHARQ_FUSED(C, NN, MM)                                                                                    \
   hipLaunchKernelGGL((linear_silu_prepare_kernel<C, NN, MM>), dim3(total), dim3(kThreads), 0, stream, op, out, \
                      tiles_m, total)

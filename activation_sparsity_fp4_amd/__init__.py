@@ -26,6 +26,9 @@ __all__ = [
     "linear_silu_prepare",
     "linear_silu_prepare_into",
     "linear_grouped_silu_prepare",
+    "CompactBackbone",
+    "compress_backbone",
+    "expand_backbone",
     "silu_mul",
     "SharqError",
     "status_string",
@@ -350,6 +353,58 @@ def linear_grouped_silu_prepare(prep: Prepared, w_gu: MXFP4, seg_offsets, a_rows
                    _ptr(hp and hp.res_scales), _ptr(hp and hp.mask), _stream(dev))
     _lib.check("sharq_linear_grouped_silu_prepare", st)
     return hp, h
+
+
+class CompactBackbone(NamedTuple):
+    """A compressed backbone: kept codes [T, K/4] (row-major), per-group rank
+    fields [T, meta_row_bytes], the n:m pattern and K. The backbone's block
+    scales stay in the Prepared it came from."""
+    codes: "object"
+    meta: "object"
+    n: int
+    m: int
+    K: int
+
+
+def compress_backbone(prep: Prepared, n: int = 2, m: int = 4, out: CompactBackbone = None) -> CompactBackbone:
+    """The compressed form of prep's backbone (needs prep.mask)."""
+    torch = _torch()
+    _check_prepared(prep)
+    if prep.mask is None:
+        raise ValueError("compressing the backbone needs the mask")
+    T, K = prep.bb_codes.shape[1], prep.K
+    row = _lib.call("sharq_backbone_meta_row_bytes", K, n, m)
+    _lib.check("sharq_backbone_meta_row_bytes", int(min(row, 0)))
+    if out is None:
+        dev = prep.bb_codes.device
+        out = CompactBackbone(torch.empty((T, K // 4), dtype=torch.uint8, device=dev),
+                              torch.empty((T, row), dtype=torch.uint8, device=dev), n, m, K)
+    if tuple(out.codes.shape) != (T, K // 4) or tuple(out.meta.shape) != (T, row) or (out.n, out.m, out.K) != (n, m, K):
+        raise ValueError("out does not match the backbone")
+    st = _lib.call("sharq_compress_backbone", prep.bb_codes.data_ptr(), prep.mask.data_ptr(), T, K, n, m,
+                   out.codes.data_ptr(), out.meta.data_ptr(), _stream(prep.bb_codes.device))
+    _lib.check("sharq_compress_backbone", st)
+    return out
+
+
+def expand_backbone(cb: CompactBackbone, bb_codes=None, mask=None, with_mask: bool = True):
+    """Dense stage-major backbone codes [G, T, 64] (and the mask [T, K/8])
+    from a CompactBackbone. Returns (bb_codes, mask or None)."""
+    torch = _torch()
+    _need(cb.codes, torch.uint8, "codes", 2)
+    _need(cb.meta, torch.uint8, "meta", 2)
+    T, K = cb.codes.shape[0], cb.K
+    dev = cb.codes.device
+    if bb_codes is None:
+        bb_codes = torch.empty((stages(K), T, 64), dtype=torch.uint8, device=dev)
+    if with_mask and mask is None:
+        mask = torch.empty((T, K // 8), dtype=torch.uint8, device=dev)
+    if not with_mask:
+        mask = None
+    st = _lib.call("sharq_expand_backbone", cb.codes.data_ptr(), cb.meta.data_ptr(), T, K, cb.n, cb.m,
+                   bb_codes.data_ptr(), _ptr(mask), _stream(dev))
+    _lib.check("sharq_expand_backbone", st)
+    return bb_codes, mask
 
 
 def silu_mul(gu, out=None):

@@ -42,6 +42,9 @@ SIGNATURES = {
                                             _P, _P, _P, _I64, _P]),
     "sharq_linear_grouped_silu_prepare": (_INT, [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _I64, _I64,
                                                  _I64, _INT, _INT, _P, _P, _P, _P, _P, _P, _P]),
+    "sharq_backbone_meta_row_bytes": (_I64, [_I64, _INT, _INT]),
+    "sharq_compress_backbone": (_INT, [_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P]),
+    "sharq_expand_backbone": (_INT, [_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P]),
     "sharq_silu_mul": (_INT, [_P, _I64, _I64, _P, _P]),
 }
 

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsharq.so")
-SOURCES = ["prepare.hip", "gemm.hip", "glue.hip", "sharq_api.hip"]
+SOURCES = ["prepare.hip", "gemm.hip", "glue.hip", "compact.hip", "sharq_api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.

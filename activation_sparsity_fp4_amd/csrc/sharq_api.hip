@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -50,6 +50,19 @@ int check_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales, const 
                 !aligned16(h_res_scales))) ||
       (h_mask && !aligned16(h_mask)))
     return SHARQ_EALIGN;
+  return SHARQ_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Shape checks of the compressed-backbone entry points.
+int check_compact(int64_t T, int64_t K, int n, int m) {
+  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
+  if (T < 0 || K <= 0 || K % 32 != 0) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31) || T * (K / 32) >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (K % 64 != 0) return SHARQ_ENOTIMPL;
   return SHARQ_OK;
 }
 
@@ -231,6 +244,31 @@ int sharq_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb
   return hip_status(sharq::launch_linear_grouped_silu_prepare(
       bb_codes, bb_scales, res_codes, res_scales, a_rows, seg_offsets, E, w_codes, w_scales, P, I, K, T_src, n, m, h,
       h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, stream));
+}
+
+int64_t sharq_backbone_meta_row_bytes(int64_t K, int n, int m) {
+  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
+  if (K <= 0 || K % 32 != 0) return SHARQ_EINVAL;
+  if (K % 64 != 0) return SHARQ_ENOTIMPL;
+  return sharq::backbone_meta_row_bytes(K, m);
+}
+
+int sharq_compress_backbone(const uint8_t* bb_codes, const uint8_t* mask, int64_t T, int64_t K, int n, int m,
+                            uint8_t* codes, uint8_t* meta, hipStream_t stream) {
+  const int rc = check_compact(T, K, n, m);
+  if (rc != SHARQ_OK || T == 0) return rc;
+  if (!bb_codes || !mask || !codes || !meta) return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(mask) || !aligned16(codes)) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_compress_backbone(bb_codes, mask, T, K, n, m, codes, meta, stream));
+}
+
+int sharq_expand_backbone(const uint8_t* codes, const uint8_t* meta, int64_t T, int64_t K, int n, int m,
+                          uint8_t* bb_codes, uint8_t* mask, hipStream_t stream) {
+  const int rc = check_compact(T, K, n, m);
+  if (rc != SHARQ_OK || T == 0) return rc;
+  if (!codes || !meta || !bb_codes) return SHARQ_EINVAL;
+  if (!aligned16(codes) || !aligned16(bb_codes) || (mask && !aligned16(mask))) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_expand_backbone(codes, meta, T, K, n, m, bb_codes, mask, stream));
 }
 
 int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {

@@ -53,6 +53,14 @@ hipError_t launch_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uin
                                               uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
                                               uint8_t* h_res_scales, uint8_t* h_mask, hipStream_t stream);
 
+int64_t backbone_meta_row_bytes(int64_t K, int m);
+
+hipError_t launch_compress_backbone(const uint8_t* bb_codes, const uint8_t* mask, int64_t T, int64_t K, int n, int m,
+                                    uint8_t* codes, uint8_t* meta, hipStream_t stream);
+
+hipError_t launch_expand_backbone(const uint8_t* codes, const uint8_t* meta, int64_t T, int64_t K, int n, int m,
+                                  uint8_t* bb_codes, uint8_t* mask, hipStream_t stream);
+
 hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream);
 
 }  // namespace sharq

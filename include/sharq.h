@@ -278,6 +278,48 @@ SHARQ_API int sharq_linear_grouped_silu_prepare(const uint8_t* bb_codes, const u
                               hipStream_t stream);
 
 /*
+ * Compressed sparse backbone -- the "sparse input compression" of the fused
+ * prepare (SharQ page, Abstract; the page gives no format). For N:M with
+ * N = M / 2 (2:4 and 8:16) a row's backbone keeps, per group of M, only its N
+ * kept codes in index order (K / 4 bytes instead of K / 2), plus one field
+ * per group: the colexicographic rank of the kept positions,
+ * C(c_1, 1) + ... + C(c_N, N) for kept c_1 < ... < c_N inside the group, in
+ * ceil(log2 C(M, N)) bits (3 for 2:4, 14 for 8:16: the 0.75 and 0.875 bits
+ * per element of the 8:16 page, abstract). A row's fields are a bit stream,
+ * group g at bits [g b, g b + b), least significant bit first. Block scales
+ * (bb_scales) are unchanged and not touched. All shapes need K % 64 == 0
+ * (SHARQ_ENOTIMPL otherwise).
+ *
+ * sharq_backbone_meta_row_bytes -- host: bytes of one row's field stream,
+ * K / 64 * 6 (2:4) or K / 64 * 7 (8:16); a negative status on bad arguments.
+ */
+SHARQ_API int64_t sharq_backbone_meta_row_bytes(int64_t K, int n, int m);
+
+/*
+ * sharq_compress_backbone -- the compressed form of a prepared backbone.
+ *  bb_codes u8 [G][T][64] (stage-major, as written by sharq_prepare) and
+ *  mask u8 [T][K/8] (required: it names the kept positions);
+ *  codes u8 [T][K/4] (row-major, two codes per byte, earlier in the low
+ *  nibble), meta u8 [T][sharq_backbone_meta_row_bytes(K, n, m)].
+ * Precondition: exactly N mask bits per group and code 0 at dropped
+ * positions (what sharq_prepare writes); otherwise the output is unspecified
+ * (no access leaves the buffers). Pointers 16-byte aligned except meta.
+ */
+SHARQ_API int sharq_compress_backbone(const uint8_t* bb_codes, const uint8_t* mask,
+                              int64_t T, int64_t K, int n, int m,
+                              uint8_t* codes, uint8_t* meta, hipStream_t stream);
+
+/*
+ * sharq_expand_backbone -- the inverse: codes and meta as above -> the dense
+ * stage-major bb_codes [G][T][64] (blocks of a last, partial stage are
+ * written as zero) and the mask [T][K/8] (or NULL to skip it). Fields of
+ * C(M, N) or more give unspecified codes and mask, still inside the buffers.
+ */
+SHARQ_API int sharq_expand_backbone(const uint8_t* codes, const uint8_t* meta,
+                              int64_t T, int64_t K, int n, int m,
+                              uint8_t* bb_codes, uint8_t* mask, hipStream_t stream);
+
+/*
  * sharq_silu_mul -- glue between a fused gate|up projection and the down
  * projection (not part of the method): h[t][i] = bf16(silu(g) * u) with
  * g = gu[t][i], u = gu[t][I + i], silu(g) = g / (1 + exp(-g)), fp32 math,

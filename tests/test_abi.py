@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 4
+    assert _lib.call("sharq_abi_version") == 5
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
@@ -243,3 +243,21 @@ def test_linear_silu_prepare_ws_validation():
     assert fused_ws(ws=0, nbytes=16) == _lib.SHARQ_EINVAL
     assert fused_ws(ws=A + 0x400004) == _lib.SHARQ_EALIGN
     assert fused_ws(h=G + 2) == _lib.SHARQ_EALIGN
+
+
+def test_compact_backbone_validation():
+    assert _lib.call("sharq_backbone_meta_row_bytes", 4096, 2, 4) == 384
+    assert _lib.call("sharq_backbone_meta_row_bytes", 14336, 8, 16) == 1568
+    assert _lib.call("sharq_backbone_meta_row_bytes", 96, 2, 4) == _lib.SHARQ_ENOTIMPL
+    assert _lib.call("sharq_backbone_meta_row_bytes", 100, 2, 4) == _lib.SHARQ_EINVAL
+    assert _lib.call("sharq_backbone_meta_row_bytes", 128, 4, 8) == _lib.SHARQ_EUNSUPPORTED
+    cmp = lambda *a: _lib.call("sharq_compress_backbone", *a)
+    exp = lambda *a: _lib.call("sharq_expand_backbone", *a)
+    assert cmp(A, B, 0, 128, 2, 4, C, D, 0) == _lib.SHARQ_OK
+    assert cmp(A, B, 4, 96, 2, 4, C, D, 0) == _lib.SHARQ_ENOTIMPL
+    assert cmp(A, 0, 4, 128, 2, 4, C, D, 0) == _lib.SHARQ_EINVAL      # the mask is required
+    assert cmp(A, B, 4, 128, 8, 16, C + 4, D, 0) == _lib.SHARQ_EALIGN
+    assert cmp(A, B, 4, 128, 3, 4, C, D, 0) == _lib.SHARQ_EUNSUPPORTED
+    assert exp(A, 0, 4, 128, 2, 4, C, D, 0) == _lib.SHARQ_EINVAL
+    assert exp(A, B, 4, 128, 2, 4, C, D + 2, 0) == _lib.SHARQ_EALIGN
+    assert exp(A, B, -1, 128, 2, 4, C, D, 0) == _lib.SHARQ_EINVAL

@@ -72,12 +72,34 @@ __device__ __forceinline__ Segment segment_of_lane(uint32_t stages, int64_t rows
   return s;
 }
 
+// C(c, i) for 0 <= c < 16, 1 <= i <= N (c and i per lane): in closed form
+// for 2:4 (i <= 2), from the workgroup's LDS copy of the table otherwise.
+template <int M>
+__device__ __forceinline__ uint32_t binom(const uint32_t* lds_table, uint32_t c, uint32_t i) {
+  if constexpr (M == 4) {
+    return i == 1 ? c : c * (c - 1) / 2;
+  } else {
+    return lds_table[c * 9 + i];
+  }
+}
+
+// Every thread of the workgroup takes part (before any early return).
+template <int M>
+__device__ __forceinline__ void load_binomials(uint32_t* lds_table) {
+  if constexpr (M != 4) {
+    for (uint32_t q = threadIdx.x; q < 17 * 9; q += blockDim.x) lds_table[q] = (&kBinom.c[0][0])[q];
+    __syncthreads();
+  }
+}
+
 template <int N, int M>
 __global__ __launch_bounds__(256) void compress_backbone_kernel(const uint8_t* __restrict__ bb_codes,
                                                                 const uint8_t* __restrict__ mask, int64_t T,
                                                                 int64_t K, uint32_t stages,
                                                                 uint8_t* __restrict__ codes_out,
                                                                 uint8_t* __restrict__ meta_out) {
+  __shared__ uint32_t table[17 * 9];
+  load_binomials<M>(table);
   const Segment sg = segment_of_lane(stages, T);
   if (!sg.row_ok || (int64_t)sg.j * 64 >= K) return;
   const int64_t t = sg.t;
@@ -87,34 +109,35 @@ __global__ __launch_bounds__(256) void compress_backbone_kernel(const uint8_t* _
   const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
   const uint2 mw = *reinterpret_cast<const uint2*>(mask + t * (K / 8) + 8 * (int64_t)sg.j);
   const uint64_t keep = (uint64_t)mw.x | ((uint64_t)mw.y << 32);
-  // kept codes in index order, 8 nibbles per output word
-  uint32_t out[4] = {0, 0, 0, 0};
-  uint32_t k = 0;
-#pragma unroll
-  for (int p = 0; p < 64; ++p) {
-    const uint32_t nib = (cw[p >> 3] >> (4 * (p & 7))) & 0xFu;
-    if ((keep >> p) & 1u) {
-      const uint32_t kk = k < 32 ? k : 31;  // a well-formed mask keeps exactly 32
-      out[kk >> 3] |= nib << (4 * (kk & 7));
-      ++k;
-    }
-  }
-  *reinterpret_cast<uint4*>(codes_out + t * (K / 4) + 16 * (int64_t)sg.j) = make_uint4(out[0], out[1], out[2], out[3]);
-  // one field per group: the colex rank of its kept positions
+  // per group: the kept positions in increasing order (lowest set bit first)
+  // give both the kept codes, in index order, and the rank C(c_1, 1) + ...
   constexpr int kB = field_bits<M>();
+  constexpr int kGroups = 64 / M;
+  uint32_t out[4] = {0, 0, 0, 0};
   uint64_t fields = 0;
 #pragma unroll
-  for (int g = 0; g < 64 / M; ++g) {
-    uint32_t rank = 0, i = 0;
+  for (int g = 0; g < kGroups; ++g) {
+    // the group's 4 M code bits, position 0 lowest
+    uint64_t gc;
+    if constexpr (M == 4) {
+      gc = (cw[g >> 1] >> (16 * (g & 1))) & 0xFFFFu;
+    } else {
+      gc = (uint64_t)cw[2 * g] | ((uint64_t)cw[2 * g + 1] << 32);
+    }
+    uint32_t gm = (uint32_t)(keep >> (g * M)) & ((1u << M) - 1);
+    uint32_t rank = 0;
 #pragma unroll
-    for (int p = 0; p < M; ++p) {
-      if ((keep >> (g * M + p)) & 1u) {
-        ++i;
-        rank += kBinom.c[p][i < 8 ? i : 8];
-      }
+    for (int i = 0; i < N; ++i) {
+      const uint32_t c = gm ? (uint32_t)__builtin_ctz(gm) : 0;  // a well-formed group has N set bits
+      gm &= gm - 1;
+      const uint32_t nib = (uint32_t)(gc >> (4 * c)) & 0xFu;
+      const int k = g * N + i;  // output nibble (compile-time)
+      out[k >> 3] |= nib << (4 * (k & 7));
+      rank += binom<M>(table, c, i + 1);
     }
     fields |= (uint64_t)(rank & ((1u << kB) - 1)) << (g * kB);
   }
+  *reinterpret_cast<uint4*>(codes_out + t * (K / 4) + 16 * (int64_t)sg.j) = make_uint4(out[0], out[1], out[2], out[3]);
   uint8_t* dst = meta_out + t * (K / 64 * segment_meta_bytes<M>()) + (int64_t)sg.j * segment_meta_bytes<M>();
 #pragma unroll
   for (int q = 0; q < segment_meta_bytes<M>(); ++q) dst[q] = (uint8_t)(fields >> (8 * q));
@@ -126,6 +149,8 @@ __global__ __launch_bounds__(256) void expand_backbone_kernel(const uint8_t* __r
                                                               int64_t K, uint32_t stages,
                                                               uint8_t* __restrict__ bb_codes,
                                                               uint8_t* __restrict__ mask) {
+  __shared__ uint32_t table[17 * 9];
+  load_binomials<M>(table);
   const Segment sg = segment_of_lane(stages, T);
   if (!sg.row_ok) return;
   const int64_t t = sg.t;
@@ -139,32 +164,42 @@ __global__ __launch_bounds__(256) void expand_backbone_kernel(const uint8_t* __r
   uint64_t fields = 0;
 #pragma unroll
   for (int q = 0; q < segment_meta_bytes<M>(); ++q) fields |= (uint64_t)src[q] << (8 * q);
-  // kept positions of each group: the largest p with C(p, i) <= rank is c_i, then i - 1 below it
-  constexpr int kB = field_bits<M>();
-  uint64_t keep = 0;
-#pragma unroll
-  for (int g = 0; g < 64 / M; ++g) {
-    uint32_t r = (uint32_t)(fields >> (g * kB)) & ((1u << kB) - 1);
-    int i = N;
-#pragma unroll
-    for (int p = M - 1; p >= 0; --p) {
-      if (i > 0 && kBinom.c[p][i] <= r) {
-        r -= kBinom.c[p][i];
-        keep |= 1ull << (g * M + p);
-        --i;
-      }
-    }
-  }
   const uint4 cin = *reinterpret_cast<const uint4*>(codes_in + t * (K / 4) + 16 * (int64_t)sg.j);
   const uint32_t kw[4] = {cin.x, cin.y, cin.z, cin.w};
+  // per group, the kept positions from the rank: scanning p = M-1 .. 0, p is
+  // the next (largest remaining) kept position c_i when C(p, i) <= the rank
+  // left; the i-th kept code (in index order) goes to position c_i
+  constexpr int kB = field_bits<M>();
+  constexpr int kGroups = 64 / M;
   uint32_t dense[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  uint32_t k = 0;
+  uint64_t keep = 0;
 #pragma unroll
-  for (int p = 0; p < 64; ++p) {
-    if ((keep >> p) & 1u) {
-      const uint32_t kk = k < 32 ? k : 31;
-      dense[p >> 3] |= ((kw[kk >> 3] >> (4 * (kk & 7))) & 0xFu) << (4 * (p & 7));
-      ++k;
+  for (int g = 0; g < kGroups; ++g) {
+    uint32_t r = (uint32_t)(fields >> (g * kB)) & ((1u << kB) - 1);
+    uint32_t i = N;
+    uint32_t gm = 0;
+#pragma unroll
+    for (int p = M - 1; p >= 0; --p) {
+      const uint32_t cb = binom<M>(table, (uint32_t)p, i > 0 ? i : 1);
+      const bool take = i > 0 && cb <= r;
+      r -= take ? cb : 0;
+      gm |= take ? 1u << p : 0u;
+      i -= take ? 1 : 0;
+    }
+    keep |= (uint64_t)gm << (g * M);
+    uint64_t gd = 0;  // the group's dense code bits
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      const uint32_t c = gm ? (uint32_t)__builtin_ctz(gm) : 0;
+      gm &= gm - 1;
+      const int k = g * N + q;  // compressed nibble (compile-time)
+      gd |= (uint64_t)((kw[k >> 3] >> (4 * (k & 7))) & 0xFu) << (4 * c);
+    }
+    if constexpr (M == 4) {
+      dense[g >> 1] |= (uint32_t)gd << (16 * (g & 1));
+    } else {
+      dense[2 * g] = (uint32_t)gd;
+      dense[2 * g + 1] = (uint32_t)(gd >> 32);
     }
   }
   *reinterpret_cast<uint4*>(bb_codes + code_offset(t, 2 * sg.j, T)) = make_uint4(dense[0], dense[1], dense[2], dense[3]);

@@ -32,7 +32,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 scaled MFMA
 
 WORKLOADS = ["llama8b_mlp", "linear_128x4096", "down_8of16", "down_2of4", "llama70b_decode_T1",
-             "llama70b_decode_T8", "llama70b_decode_T32", "llama70b_decode_T64", "qwen3_moe"]
+             "llama70b_decode_T8", "llama70b_decode_T32", "llama70b_decode_T64", "qwen3_moe", "compact_2of4",
+             "compact_8of16"]
 
 
 def prepare_bytes(T, K, gamma=False):
@@ -158,6 +159,29 @@ def build_workload(name, torch, sq, unfused=False):
             return time.perf_counter() - t0
         return stages, T, cfg, oracle_sample
 
+    if name.startswith("compact_"):
+        # compressed backbone of the down projection's input: prepare, compress, expand
+        wl = workload_down_silu()
+        xb = wl["x"]
+        n, m = (8, 16) if name == "compact_8of16" else (2, 4)
+        T, K = xb.shape
+        x = _to_gpu_bf16(torch, xb)
+        buf = {"p": sq.prepare(x, None, n, m)}
+        buf["c"] = sq.compress_backbone(buf["p"], n, m)
+        buf["bb"], buf["mask"] = sq.expand_backbone(buf["c"])
+        meta = buf["c"].meta.shape[1]
+        dense = T * K * (0.5 + 1 / 8)            # dense backbone codes + mask
+        packed = T * (K / 4 + meta)              # kept codes + rank fields
+        stages = [Stage("prepare", lambda: sq.prepare(x, None, n, m, out=buf["p"]), "hbm", prepare_bytes(T, K)),
+                  Stage("compress_backbone", lambda: sq.compress_backbone(buf["p"], n, m, out=buf["c"]), "hbm",
+                        dense + packed),
+                  Stage("expand_backbone", lambda: sq.expand_backbone(buf["c"], buf["bb"], buf["mask"]), "hbm",
+                        dense + packed)]
+        cfg = {"workload": f"compressed sparse backbone of the down_proj input 2048x14336, {n}:{m}", "tokens": T,
+               "in_features": K, "nm": f"{n}:{m}",
+               "backbone_bytes_per_element": {"dense_codes_and_mask": 0.625, "compressed": round(packed / (T * K), 4)}}
+        return stages, T, cfg, None
+
     if name.startswith("llama70b_decode_T"):
         T = int(name.split("_T")[1])
         wl = workload_llama70b_decode(T)
@@ -245,7 +269,7 @@ def build_workload(name, torch, sq, unfused=False):
 
 
 KERNEL_SOURCES = {"gemm": ["gemm.hip"], "prepare": ["prepare.hip"], "silu": ["glue.hip", "silu.h"],
-                  "grouped": ["gemm.hip"]}
+                  "grouped": ["gemm.hip"], "compact": ["compact.hip"]}
 SHARED_HEADERS = ["sharq_device.h", "prepare_block.h", "sort_network.h", "silu.h"]
 
 
@@ -254,7 +278,7 @@ def source_digest(stage_name):
     they include (ties recorded counters to a kernel version)."""
     import hashlib
     key = "gemm" if "gemm" in stage_name or "grouped" in stage_name else (
-        "silu" if "silu" in stage_name else "prepare")
+        "silu" if "silu" in stage_name else "compact" if "backbone" in stage_name else "prepare")
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[key] + SHARED_HEADERS:
         with open(os.path.join(ROOT, "activation_sparsity_fp4_amd", "csrc", name), "rb") as f:

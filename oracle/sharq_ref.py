@@ -77,6 +77,7 @@ __all__ = [
     "linear_ref",
     "linear_grouped_ref",
     "silu_mul_ref",
+    "moe_combine_ref",
 ]
 
 # E2M1 magnitudes indexed by the 3-bit code (bit 3 of a code is the sign).
@@ -494,3 +495,24 @@ def silu_mul_ref(gu: np.ndarray, inter: int) -> np.ndarray:
     with np.errstate(over="ignore"):
         h = g / (1.0 + np.exp(-g)) * u
     return f64_to_bf16_bits_rne(h)
+
+
+def moe_combine_ref(y: np.ndarray, pair_index: np.ndarray, weights: np.ndarray):
+    """Weighted combine of a mixture-of-experts layer (glue around the grouped
+    two-path GEMM; the SharQ page, Abstract, names MoE models as targets):
+    out[t] = sum over slots j of weights[t, j] * y[pair_index[t, j]], skipping
+    slots with pair_index -1, in float64. Returns (out [T, H] float64, bound
+    [T, H] = sum_j |weights[t, j] * y[pair_index[t, j]]|)."""
+    y = np.asarray(y, dtype=np.float64)
+    idx = np.asarray(pair_index)
+    w = np.asarray(weights, dtype=np.float64)
+    _require_finite(y, "y")
+    T, k = idx.shape
+    out = np.zeros((T, y.shape[1]))
+    bound = np.zeros((T, y.shape[1]))
+    for j in range(k):
+        ok = idx[:, j] >= 0
+        term = w[ok, j][:, None] * y[idx[ok, j]]
+        out[ok] += term
+        bound[ok] += np.abs(term)
+    return out, bound

@@ -37,6 +37,7 @@ __all__ = [
     "workload_llama70b_decode",
     "workload_qwen3_moe",
     "moe_routing",
+    "moe_combine_index",
     "array_digest",
     "adversarial_rows",
 ]
@@ -157,6 +158,26 @@ def moe_routing(rng, tokens: int, experts: int, top_k: int):
     seg = np.zeros(experts + 1, dtype=np.int32)
     seg[1:] = np.cumsum(counts)
     return a_rows, seg, e_sorted, wts.reshape(-1)[srt].astype(np.float32)
+
+
+def moe_combine_index(a_rows: np.ndarray, weight_of_pair: np.ndarray, tokens: int, top_k: int):
+    """Token-major view of a routing (indexing only): pair_index [tokens, top_k]
+    int32 lists the sorted pairs of each token in sorted-pair order (-1 for an
+    empty slot), weights [tokens, top_k] float32 their routing weights (0 for an
+    empty slot)."""
+    a_rows = np.asarray(a_rows)
+    order = np.argsort(a_rows, kind="stable")  # pairs grouped by token, sorted-pair order inside
+    counts = np.bincount(a_rows, minlength=tokens)
+    if counts.max(initial=0) > top_k:
+        raise ValueError("a token has more pairs than top_k")
+    pair_index = np.full((tokens, top_k), -1, dtype=np.int32)
+    weights = np.zeros((tokens, top_k), dtype=np.float32)
+    start = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    slot = np.arange(len(order)) - np.repeat(start, counts)
+    tok = a_rows[order]
+    pair_index[tok, slot] = order.astype(np.int32)
+    weights[tok, slot] = np.asarray(weight_of_pair, dtype=np.float32)[order]
+    return pair_index, weights
 
 
 def workload_qwen3_moe(seed: int = SEEDS["qwen3_moe"], tokens: int = 4096, hidden: int = 2048,

@@ -29,6 +29,7 @@ __all__ = [
     "CompactBackbone",
     "compress_backbone",
     "expand_backbone",
+    "moe_combine",
     "silu_mul",
     "SharqError",
     "status_string",
@@ -405,6 +406,29 @@ def expand_backbone(cb: CompactBackbone, bb_codes=None, mask=None, with_mask: bo
                    bb_codes.data_ptr(), _ptr(mask), _stream(dev))
     _lib.check("sharq_expand_backbone", st)
     return bb_codes, mask
+
+
+def moe_combine(y, pair_index, weights, out=None, bf16: bool = False):
+    """out[t] = sum_j weights[t, j] * y[pair_index[t, j]] (slots with -1 skipped),
+    fp32 accumulation in slot order; fp32 [T, H] or, with bf16, bf16 [T, H]."""
+    torch = _torch()
+    _need(y, torch.float32, "y", 2)
+    _need(pair_index, torch.int32, "pair_index", 2)
+    _need(weights, torch.float32, "weights", 2)
+    if not (y.is_contiguous() and pair_index.is_contiguous() and weights.is_contiguous()):
+        raise ValueError("y, pair_index and weights must be contiguous")
+    if pair_index.shape != weights.shape:
+        raise ValueError("pair_index and weights must have the same [T, k] shape")
+    T, k = pair_index.shape
+    P, H = y.shape
+    dt = torch.bfloat16 if bf16 else torch.float32
+    if out is None:
+        out = torch.empty((T, H), dtype=dt, device=y.device)
+    _need(out, dt, "out", 2)
+    st = _lib.call("sharq_moe_combine", y.data_ptr(), P, H, pair_index.data_ptr(), weights.data_ptr(), T, k,
+                   0 if bf16 else out.data_ptr(), out.data_ptr() if bf16 else 0, _stream(y.device))
+    _lib.check("sharq_moe_combine", st)
+    return out
 
 
 def silu_mul(gu, out=None):

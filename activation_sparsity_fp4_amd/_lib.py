@@ -45,6 +45,7 @@ SIGNATURES = {
     "sharq_backbone_meta_row_bytes": (_I64, [_I64, _INT, _INT]),
     "sharq_compress_backbone": (_INT, [_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P]),
     "sharq_expand_backbone": (_INT, [_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P]),
+    "sharq_moe_combine": (_INT, [_P, _I64, _I64, _P, _P, _I64, ctypes.c_int32, _P, _P, _P]),
     "sharq_silu_mul": (_INT, [_P, _I64, _I64, _P, _P]),
 }
 

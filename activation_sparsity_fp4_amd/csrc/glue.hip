@@ -31,7 +31,50 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
   reinterpret_cast<uint4*>(h + (int64_t)t * I)[c] = make_uint4(out[0], out[1], out[2], out[3]);
 }
 
+// Weighted combine of a mixture-of-experts layer (glue, not the method):
+// out[t][c] = sum over slots j = 0, 1, ..., k-1 of weights[t][j] *
+// y[pair_index[t][j]][c] (slots with index -1 skipped), accumulated in fp32
+// in slot order with one fused multiply-add per slot, so the result does not
+// depend on timing. A lane owns 4 columns of one token row: HBM-bound, k
+// gathered 16-byte reads and one 16-byte (fp32) or 8-byte (bf16) write.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ y, int64_t H,
+                                                          const int32_t* __restrict__ pair_index,
+                                                          const float* __restrict__ weights, int k,
+                                                          uint32_t quads_per_row, uint32_t total,
+                                                          float* __restrict__ out, uint16_t* __restrict__ out_bf16) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const uint32_t t = gid / quads_per_row;
+  const uint32_t c = gid - t * quads_per_row;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int32_t p = pair_index[(int64_t)t * k + j];
+    if (p < 0) continue;
+    const float w = weights[(int64_t)t * k + j];
+    const float4 v = reinterpret_cast<const float4*>(y + (int64_t)p * H)[c];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  if (out) reinterpret_cast<float4*>(out + (int64_t)t * H)[c] = acc;
+  if (out_bf16) {
+    const uint32_t lo = bf16_rne_bits(acc.x) | (bf16_rne_bits(acc.y) << 16);
+    const uint32_t hi = bf16_rne_bits(acc.z) | (bf16_rne_bits(acc.w) << 16);
+    reinterpret_cast<uint2*>(out_bf16 + (int64_t)t * H)[c] = make_uint2(lo, hi);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_moe_combine(const float* y, int64_t H, const int32_t* pair_index, const float* weights, int64_t T,
+                              int k, float* out, uint16_t* out_bf16, hipStream_t stream) {
+  const uint32_t qpr = (uint32_t)(H / 4);
+  const uint32_t total = (uint32_t)(T * qpr);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, y, H, pair_index, weights,
+                     k, qpr, total, out, out_bf16);
+  return hipGetLastError();
+}
 
 hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {
   const uint32_t gpr = (uint32_t)(I / 8);

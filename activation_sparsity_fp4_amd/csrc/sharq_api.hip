@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -269,6 +269,19 @@ int sharq_expand_backbone(const uint8_t* codes, const uint8_t* meta, int64_t T, 
   if (!codes || !meta || !bb_codes) return SHARQ_EINVAL;
   if (!aligned16(codes) || !aligned16(bb_codes) || (mask && !aligned16(mask))) return SHARQ_EALIGN;
   return hip_status(sharq::launch_expand_backbone(codes, meta, T, K, n, m, bb_codes, mask, stream));
+}
+
+int sharq_moe_combine(const float* y, int64_t P, int64_t H, const int32_t* pair_index, const float* weights,
+                      int64_t T, int32_t k, float* out, uint16_t* out_bf16, hipStream_t stream) {
+  if (P < 0 || H <= 0 || H % 4 != 0 || T < 0 || k < 1 || k > 64) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || T * (H / 4) >= ((int64_t)1 << 32) - 256) return SHARQ_EINVAL;  // 32-bit lane index
+  if (!out && !out_bf16) return SHARQ_EINVAL;  // nothing to write
+  if (T == 0) return SHARQ_OK;
+  if (!pair_index || !weights || (P > 0 && !y)) return SHARQ_EINVAL;
+  if ((y && !aligned16(y)) || (out && !aligned16(out)) || (out_bf16 && ((uintptr_t)out_bf16 & 7u)) ||
+      ((uintptr_t)pair_index & 3u) || ((uintptr_t)weights & 3u))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_moe_combine(y, H, pair_index, weights, T, k, out, out_bf16, stream));
 }
 
 int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {

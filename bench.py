@@ -253,13 +253,21 @@ def build_workload(name, torch, sq, unfused=False):
                       gu_in_bytes + prepare_bytes(P, I) - 2 * P * I, fa1, fe1),
             ]
         buf["y"] = sq.linear_grouped(buf["p2"], w_dn, seg, None)
+        from synth import moe_combine_index
+        k = P // tokens
+        cidx, cw = moe_combine_index(wl["a_rows"], wl["weight_of_pair"], tokens, k)
+        cidx, cw = torch.from_numpy(cidx).cuda(), torch.from_numpy(cw).cuda()
+        buf["out"] = sq.moe_combine(buf["y"], cidx, cw, bf16=True)
         stages = [
             Stage("prepare_tokens", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(tokens, H))
         ] + middle + [
             Stage("grouped_down", lambda: sq.linear_grouped(buf["p2"], w_dn, seg, None, out=buf["y"]), "hbm",
                   2 * P * I * 17 / 32 + E * H * I * 17 / 32 + 4 * P * H, fa2, fe2),
+            Stage("moe_combine", lambda: sq.moe_combine(buf["y"], cidx, cw, out=buf["out"], bf16=True), "hbm",
+                  4 * P * H + 2 * tokens * H + 8 * P),
         ]
-        cfg = {"workload": "Qwen3-30B-A3B MoE expert layer, 4096 tokens, top-8 of 128, 2:4, MXFP4",
+        cfg = {"workload": "Qwen3-30B-A3B MoE expert layer, 4096 tokens, top-8 of 128, 2:4, MXFP4, weighted "
+                           "combine to bf16 tokens",
                "tokens": tokens, "pairs": P, "experts": E, "hidden": H, "intermediate": I, "nm": "2:4",
                "gate_up": "unfused (linear_grouped, silu_mul, prepare)" if unfused
                else "fused (linear_grouped_silu_prepare)"}

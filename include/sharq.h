@@ -320,6 +320,27 @@ SHARQ_API int sharq_expand_backbone(const uint8_t* codes, const uint8_t* meta,
                               uint8_t* bb_codes, uint8_t* mask, hipStream_t stream);
 
 /*
+ * sharq_moe_combine -- the weighted combine of a mixture-of-experts layer
+ * (glue around sharq_linear_grouped, not part of the method; the SharQ
+ * page, Abstract, names MoE models among the targets):
+ *   out[t][c] = sum_{j = 0 .. k-1, pair_index[t][j] >= 0} weights[t][j] * y[pair_index[t][j]][c]
+ * accumulated in fp32 in slot order j = 0, 1, ... with one fused
+ * multiply-add per slot (deterministic).
+ *  y           fp32 [P][H], the grouped GEMM's output rows (sorted pairs);
+ *  pair_index  i32 [T][k], the pairs of token t (-1: empty slot; each in
+ *              [0, P) otherwise, a precondition read on the device);
+ *  weights     fp32 [T][k];
+ *  out         fp32 [T][H] or NULL; out_bf16 bf16 [T][H] (the fp32 sum
+ *              rounded to nearest even) or NULL; at least one is given.
+ * Requires H % 4 == 0 and 1 <= k <= 64; y and out 16-byte aligned, out_bf16
+ * 8-byte aligned, pair_index and weights 4-byte aligned.
+ */
+SHARQ_API int sharq_moe_combine(const float* y, int64_t P, int64_t H,
+                              const int32_t* pair_index, const float* weights,
+                              int64_t T, int32_t k, float* out, uint16_t* out_bf16,
+                              hipStream_t stream);
+
+/*
  * sharq_silu_mul -- glue between a fused gate|up projection and the down
  * projection (not part of the method): h[t][i] = bf16(silu(g) * u) with
  * g = gu[t][i], u = gu[t][I + i], silu(g) = g / (1 + exp(-g)), fp32 math,

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 5
+    assert _lib.call("sharq_abi_version") == 6
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
@@ -261,3 +261,15 @@ def test_compact_backbone_validation():
     assert exp(A, 0, 4, 128, 2, 4, C, D, 0) == _lib.SHARQ_EINVAL
     assert exp(A, B, 4, 128, 2, 4, C, D + 2, 0) == _lib.SHARQ_EALIGN
     assert exp(A, B, -1, 128, 2, 4, C, D, 0) == _lib.SHARQ_EINVAL
+
+
+def test_moe_combine_validation():
+    call = lambda *a: _lib.call("sharq_moe_combine", *a)
+    assert call(A, 8, 16, B, C, 0, 2, D, 0, 0) == _lib.SHARQ_OK
+    assert call(A, 8, 18, B, C, 4, 2, D, 0, 0) == _lib.SHARQ_EINVAL       # H % 4
+    assert call(A, 8, 16, B, C, 4, 0, D, 0, 0) == _lib.SHARQ_EINVAL       # k >= 1
+    assert call(A, 8, 16, B, C, 4, 2, 0, 0, 0) == _lib.SHARQ_EINVAL       # no output
+    assert call(A, 8, 16, 0, C, 4, 2, D, 0, 0) == _lib.SHARQ_EINVAL
+    assert call(A + 4, 8, 16, B, C, 4, 2, D, 0, 0) == _lib.SHARQ_EALIGN
+    assert call(A, 8, 16, B, C, 4, 2, 0, D + 4, 0) == _lib.SHARQ_EALIGN   # bf16 output needs 8 bytes
+    assert call(A, 8, 16, B + 2, C, 4, 2, D, 0, 0) == _lib.SHARQ_EALIGN

@@ -150,3 +150,37 @@ def test_qwen3_moe_layer_chain(sq):
         assert_y_close(y_np[pp:pp + 1, dcols], yr, b)
     want_h = silu_mul_ref(gu_np[pairs], I)
     assert_bf16_close(h_np[pairs], want_h)
+
+
+def test_moe_combine_small_and_qwen3_size(sq):
+    """Weighted combine: fp32 sums in slot order against the float64 oracle
+    (bound 2 k 2^-24 sum|w y| per element), empty slots, and the bf16 output
+    equal to the fp32 output rounded to nearest even (the oracle's rounding)."""
+    import torch
+    from oracle import f32_to_bf16_bits_rne, moe_combine_ref
+    from synth import moe_combine_index
+    print("moe combine small", flush=True)
+    rng = np.random.default_rng(14)
+    y = (rng.standard_normal((60, 32)) * rng.lognormal(0, 2, (60, 1))).astype(np.float32)
+    idx = rng.integers(-1, 60, (23, 5)).astype(np.int32)
+    w = rng.uniform(-1, 1, (23, 5)).astype(np.float32)
+    yg = torch.from_numpy(y).cuda()
+    out = to_np(sq.moe_combine(yg, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()))
+    ref, bound = moe_combine_ref(y, idx, w)
+    assert np.all(np.abs(out - ref) <= 2 * 5 * 2.0 ** -24 * bound + 1e-30)
+    outb = to_np(sq.moe_combine(yg, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), bf16=True))
+    assert np.array_equal(outb, f32_to_bf16_bits_rne(out))
+    # the Qwen3-30B-A3B layer: 4096 tokens x top-8 over 32768 sorted pairs, H = 2048
+    print("moe combine qwen3 size", flush=True)
+    wl = workload_qwen3_moe(with_weights=False)
+    T, k, H = wl["x"].shape[0], 8, wl["hidden"]
+    idx, w = moe_combine_index(wl["a_rows"], wl["weight_of_pair"], T, k)
+    g = torch.Generator(device="cuda").manual_seed(15)
+    yg = torch.randn(len(wl["a_rows"]), H, device="cuda", generator=g)
+    out = to_np(sq.moe_combine(yg, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()))
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 50, replace=False)]))
+    sub = idx[toks]
+    y_np = to_np(yg[torch.from_numpy(np.unique(sub)).cuda().long()])
+    remap = {p: i for i, p in enumerate(np.unique(sub))}
+    ref, bound = moe_combine_ref(y_np, np.vectorize(remap.get)(sub).astype(np.int32), w[toks])
+    assert np.all(np.abs(out[toks] - ref) <= 2 * k * 2.0 ** -24 * bound + 1e-30)

@@ -58,36 +58,47 @@ constexpr int kRowBytes = 64;            // 128 FP4 codes
 constexpr int kLdsBytes = 160 * 1024;    // LDS of one CU
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every bound: reads as 0
 
-// Workgroup tile of 2 x 2 waves, each WM x WN MFMA tiles of 32 x 32, and the
-// layout of one LDS stage: backbone codes, residual codes, weight codes, then
-// the three scale runs (in that order, contiguous).
-template <int WM_, int WN_, int RING_>
+// Workgroup tile of NWM x 2 waves (NWM along the rows), each WM x WN MFMA
+// tiles of 32 x 32, and the layout of one LDS stage: backbone codes, residual
+// codes, weight codes, then the three scale runs (in that order; each
+// activation scale run is padded to a multiple of 64 rows, the width of one
+// buffer->LDS load).
+template <int WM_, int WN_, int RING_, int NWM_ = 2>
 struct Tile {
-  static constexpr int WM = WM_, WN = WN_;
-  static constexpr int BM = 64 * WM, BN = 64 * WN;
+  static constexpr int WM = WM_, WN = WN_, NWM = NWM_;
+  static constexpr int kWaves = 2 * NWM, kThreads = 64 * kWaves;
+  static constexpr int BM = 32 * WM * NWM, BN = 64 * WN;
+  static constexpr int kARunRows = (BM + 63) / 64 * 64;  // rows of one activation scale run
   static constexpr int kOffAs = 0;
   static constexpr int kOffAr = BM * kRowBytes;
   static constexpr int kOffW = 2 * BM * kRowBytes;
   static constexpr int kOffSAs = kOffW + BN * kRowBytes;
-  static constexpr int kOffSAr = kOffSAs + BM * 4;
-  static constexpr int kOffSW = kOffSAr + BM * 4;
+  static constexpr int kOffSAr = kOffSAs + kARunRows * 4;
+  static constexpr int kOffSW = kOffSAr + kARunRows * 4;
   // buffer->LDS instructions per wave per stage: 1 KB code chunks of each
   // activation operand, of the weight, and 256-byte scale runs (64 rows).
   // When the scale runs do not split evenly over the four waves, the spare
   // instructions read nothing (out of range) into a trash area, so that every
   // wave issues the same number of loads per stage.
-  static constexpr int kAChunks = BM / 64;
-  static constexpr int kWChunks = BN / 64;
-  static constexpr int kSRuns = (2 * BM + BN) / 64;
-  static constexpr int kSLoads = (kSRuns + 3) / 4;
+  static constexpr int kAChunks = BM / 16 / kWaves;
+  static constexpr int kWChunks = BN / 16 / kWaves;
+  static constexpr int kSRuns = (2 * kARunRows + BN) / 64;
+  static constexpr int kSLoads = (kSRuns + kWaves - 1) / kWaves;
   static constexpr int kLoads = 2 * kAChunks + kWChunks + kSLoads;
-  static constexpr int kStage = kOffSW + BN * 4 + 256 * (4 * kSLoads - kSRuns);
+  static constexpr int kStage = kOffSW + BN * 4 + 256 * (kWaves * kSLoads - kSRuns);
+  static_assert(kAChunks * 16 * kWaves == BM && kWChunks * 16 * kWaves == BN, "whole 1 KB chunks per wave");
   static constexpr int kRing = RING_;
   static constexpr int kOccupancy = kLdsBytes / (kRing * kStage);  // workgroups per CU (LDS bound)
   static_assert(kRing >= 2 && kRing * kStage <= kLdsBytes, "ring");
 };
 using SmallTile = Tile<2, 4, 2>;  // 128 x 256, 34 KB stages, ring of 2, two workgroups per CU
 using DeepTile = Tile<2, 4, 4>;   // 128 x 256, ring of 4, one workgroup per CU
+// Decode-sized T: 32 x 256 (T <= 32) and 64 x 256 (T <= 64) tiles of two
+// waves, ring of 3, two workgroups per CU. A 128-row tile runs up to 4x the
+// MFMA work on zero rows, which at T = 1 took longer than streaming the
+// weight (Llama-3.1-70B decode step 0.127 -> 0.097 ms at T = 1).
+using DecodeTile = Tile<1, 4, 3, 1>;
+using Decode64Tile = Tile<2, 4, 3, 1>;
 
 // LDS chunk swizzle. gfx950 LDS has 64 four-byte banks; a ds_read_b128 of an
 // MFMA fragment serves 16 lanes (16 consecutive rows, one 16-byte chunk each)
@@ -306,13 +317,13 @@ struct RingLoader {
   __device__ __forceinline__ void issue_j(const Dest& d) const {
     if constexpr (J < 2 * C::kAChunks) {
       constexpr int j = J / 2, p = J % 2;
-      buffer_to_lds16(a_codes[p], a_off[j] + d.ka, d.base + (p ? C::kOffAr : C::kOffAs) + 1024 * (wave + 4 * j));
+      buffer_to_lds16(a_codes[p], a_off[j] + d.ka, d.base + (p ? C::kOffAr : C::kOffAs) + 1024 * (wave + C::kWaves * j));
     } else if constexpr (J < 2 * C::kAChunks + C::kWChunks) {
       constexpr int j = J - 2 * C::kAChunks;
-      buffer_to_lds16(w_codes, w_off[j] + d.kw, d.base + C::kOffW + 1024 * (wave + 4 * j));
+      buffer_to_lds16(w_codes, w_off[j] + d.kw, d.base + C::kOffW + 1024 * (wave + C::kWaves * j));
     } else if constexpr (J < C::kLoads) {
       constexpr int i = J - 2 * C::kAChunks - C::kWChunks;
-      buffer_to_lds4(s_rsrc[i], s_off[i] + (s_is_w[i] ? d.ksw : d.ksa), d.base + C::kOffSAs + 256 * (wave + 4 * i));
+      buffer_to_lds4(s_rsrc[i], s_off[i] + (s_is_w[i] ? d.ksw : d.ksa), d.base + C::kOffSAs + 256 * (wave + C::kWaves * i));
     }
   }
 
@@ -418,7 +429,7 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::NWM, wn = wave / C::NWM;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t G = op.nsteps;
 
@@ -436,14 +447,14 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   // chunk); pick the global 16-byte chunk that belongs there after the swizzle.
 #pragma unroll
   for (int j = 0; j < C::kAChunks; ++j) {
-    const int row = 16 * (wave + 4 * j) + (lane >> 2);
+    const int row = 16 * (wave + C::kWaves * j) + (lane >> 2);
     const int part = (lane & 3) ^ swz_part(row);
     const int64_t src = tr.src(row);
     ld.a_off[j] = src >= 0 ? (uint32_t)(src * kRowBytes + part * 16) : kOOB;
   }
 #pragma unroll
   for (int j = 0; j < C::kWChunks; ++j) {
-    const int row = 16 * (wave + 4 * j) + (lane >> 2);
+    const int row = 16 * (wave + C::kWaves * j) + (lane >> 2);
     const int part = (lane & 3) ^ swz_part(row);
     const int64_t o = tc.w_row(row);
     ld.w_off[j] = o < op.O ? (uint32_t)(o * kRowBytes + part * 16) : kOOB;
@@ -451,8 +462,8 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   // scale runs: 64-row run q of [backbone rows | residual rows | weight rows]
 #pragma unroll
   for (int i = 0; i < C::kSLoads; ++i) {
-    const int q = wave + 4 * i;
-    constexpr int qa = C::BM / 64;
+    const int q = wave + C::kWaves * i;
+    constexpr int qa = C::kARunRows / 64;
     if (q >= C::kSRuns) {  // spare instruction: reads nothing, lands in the trash area
       ld.s_rsrc[i] = ws_rsrc;
       ld.s_off[i] = kOOB;
@@ -621,7 +632,7 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[C::WM][C::WN], floa
                                            int64_t m0, int64_t rows_valid, int64_t n0, int64_t O) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::NWM, wn = wave / C::NWM;
   const int lr = lane & 31, lh = lane >> 5;
   const bool full = rows_valid == C::BM && n0 + C::BN <= O;
   float* base = y + (m0 + 32 * C::WM * wm + 4 * lh) * ldy + n0 + 32 * C::WN * wn + lr;
@@ -675,7 +686,7 @@ __device__ __forceinline__ TileIndex tile_index(int b, int tiles_m, int tiles_to
 
 // Plain two-path GEMM, tiles in tile_index order.
 template <class C, bool kRingPath>
-__global__ __launch_bounds__(kThreads, kRingPath ? C::kOccupancy : 1) void linear_kernel(Operands op, int64_t T, float* __restrict__ y,
+__global__ __launch_bounds__(C::kThreads, kRingPath ? C::kOccupancy : 1) void linear_kernel(Operands op, int64_t T, float* __restrict__ y,
                                                           int64_t ldy, int tiles_m, int tiles_total) {
   SHARQ_GEMM_LDS(C, kRingPath)
   const TileIndex ti = tile_index(blockIdx.x, tiles_m, tiles_total);
@@ -702,7 +713,7 @@ __global__ __launch_bounds__(kThreads, kRingPath ? C::kOccupancy : 1) void linea
 // kernel boundary between the two launches makes the partials visible to
 // every XCD.
 template <class C>
-__global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_split_kernel(Operands op, int64_t T,
+__global__ __launch_bounds__(C::kThreads, C::kOccupancy) void linear_split_kernel(Operands op, int64_t T,
                                                                               int tiles_m, int tiles_total, int S,
                                                                               float* __restrict__ partials) {
   SHARQ_GEMM_LDS(C, true)
@@ -907,7 +918,7 @@ __device__ __forceinline__ void silu_prepare_epilogue(const v16f (&acc)[2][4], u
 template <class C, int N, int M>
 __global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_kernel(Operands op, HOutputs out,
                                                                                       int tiles_m, int tiles_total) {
-  static_assert(C::WM == 2 && C::WN == 4, "the epilogue assumes 128 x 256 tiles");
+  static_assert(C::WM == 2 && C::WN == 4 && C::NWM == 2, "the epilogue assumes 128 x 256 tiles of 2 x 2 waves");
   static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
   SHARQ_GEMM_LDS(C, true)
   const TileIndex ti = tile_index(blockIdx.x, tiles_m, tiles_total);
@@ -1043,7 +1054,7 @@ void launch_tiles(const Operands& op, int64_t T, float* y, int64_t ldy, hipStrea
   const int tiles_m = (int)((T + C::BM - 1) / C::BM);
   const int tiles_n = (int)((op.O + C::BN - 1) / C::BN);
   const int total = tiles_m * tiles_n;
-  hipLaunchKernelGGL((linear_kernel<C, kRingPath>), dim3(total), dim3(kThreads), 0, stream, op, T, y, ldy, tiles_m,
+  hipLaunchKernelGGL((linear_kernel<C, kRingPath>), dim3(total), dim3(C::kThreads), 0, stream, op, T, y, ldy, tiles_m,
                      total);
 }
 
@@ -1056,16 +1067,26 @@ void launch_tiles(const Operands& op, int64_t T, float* y, int64_t ldy, hipStrea
 // partials outweigh its weight.
 constexpr int64_t kSplitMaxRows = 256;
 
+// The tile of a problem with T rows on the ring path: 0 SmallTile (or
+// DeepTile), 1 DecodeTile, 2 Decode64Tile.
+int row_tile(int64_t T) { return T <= DecodeTile::BM ? 1 : T <= Decode64Tile::BM ? 2 : 0; }
+int64_t row_tile_bm(int tile) {
+  return tile == 1 ? DecodeTile::BM : tile == 2 ? Decode64Tile::BM : SmallTile::BM;
+}
+
 struct SplitPlan {
   int S;             // 1: no split
+  int tile;          // row_tile(T)
   int tiles_m, tiles_total;
   int64_t partial_bytes;
 };
 
 SplitPlan split_plan(int64_t T, int64_t O, int64_t K) {
-  SplitPlan p{1, 0, 0, 0};
+  SplitPlan p{1, 0, 0, 0, 0};
   if (T <= 0 || T > kSplitMaxRows || O <= 0 || T * O >= ((int64_t)1 << 31) || !ring_path_ok(T, O, K)) return p;
-  p.tiles_m = (int)((T + SmallTile::BM - 1) / SmallTile::BM);
+  p.tile = row_tile(T);
+  const int64_t bm = row_tile_bm(p.tile);
+  p.tiles_m = (int)((T + bm - 1) / bm);
   p.tiles_total = p.tiles_m * (int)((O + SmallTile::BN - 1) / SmallTile::BN);
   const int64_t nsteps = K / 128;
   int64_t S = kTwoPerCu / p.tiles_total;
@@ -1079,6 +1100,18 @@ SplitPlan split_plan(int64_t T, int64_t O, int64_t K) {
   p.S = (int)S;
   p.partial_bytes = S * T * O * 4;
   return p;
+}
+
+void launch_split(const SplitPlan& p, const Operands& op, int64_t T, float* partials, hipStream_t stream) {
+  if (p.tile == 1)
+    hipLaunchKernelGGL((linear_split_kernel<DecodeTile>), dim3(p.tiles_total * p.S), dim3(DecodeTile::kThreads), 0,
+                       stream, op, T, p.tiles_m, p.tiles_total, p.S, partials);
+  else if (p.tile == 2)
+    hipLaunchKernelGGL((linear_split_kernel<Decode64Tile>), dim3(p.tiles_total * p.S), dim3(Decode64Tile::kThreads),
+                       0, stream, op, T, p.tiles_m, p.tiles_total, p.S, partials);
+  else
+    hipLaunchKernelGGL((linear_split_kernel<SmallTile>), dim3(p.tiles_total * p.S), dim3(SmallTile::kThreads), 0,
+                       stream, op, T, p.tiles_m, p.tiles_total, p.S, partials);
 }
 
 }  // namespace
@@ -1097,8 +1130,7 @@ hipError_t launch_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, c
     return launch_linear(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K, y, ldy, stream);
   const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K);
   float* partials = static_cast<float*>(workspace);
-  hipLaunchKernelGGL((linear_split_kernel<SmallTile>), dim3(p.tiles_total * p.S), dim3(kThreads), 0, stream, op, T,
-                     p.tiles_m, p.tiles_total, p.S, partials);
+  launch_split(p, op, T, partials, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((T * O + 255) / 256)), dim3(256), 0, stream, partials,
@@ -1113,6 +1145,10 @@ hipError_t launch_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, cons
   const int64_t tiles = ((T + SmallTile::BM - 1) / SmallTile::BM) * ((O + SmallTile::BN - 1) / SmallTile::BN);
   if (!ring_path_ok(T, O, K))
     launch_tiles<SmallTile, false>(op, T, y, ldy, stream);
+  else if (row_tile(T) == 1)
+    launch_tiles<DecodeTile, true>(op, T, y, ldy, stream);
+  else if (row_tile(T) == 2)
+    launch_tiles<Decode64Tile, true>(op, T, y, ldy, stream);
   else if (tiles >= kSmallTileMin)
     launch_tiles<SmallTile, true>(op, T, y, ldy, stream);
   else
@@ -1152,8 +1188,7 @@ hipError_t launch_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t*
                                       h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, stream);
   const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, 2 * I, K);
   float* partials = static_cast<float*>(workspace);
-  hipLaunchKernelGGL((linear_split_kernel<SmallTile>), dim3(p.tiles_total * p.S), dim3(kThreads), 0, stream, op, T,
-                     p.tiles_m, p.tiles_total, p.S, partials);
+  launch_split(p, op, T, partials, stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const HOutputs out{h, h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, T, I};

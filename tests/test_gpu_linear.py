@@ -38,8 +38,11 @@ def _random_problem(T, O, K, seed, n=2, m=4):
 
 
 @pytest.mark.parametrize("T,O,K", [(37, 70, 352), (300, 600, 1024), (1, 1, 32), (129, 257, 160),
-                                   (128, 256, 128), (200, 513, 4096)])
+                                   (128, 256, 128), (200, 513, 4096), (20, 700, 512), (32, 300, 256),
+                                   (1, 256, 128), (48, 700, 512), (64, 256, 256)])
 def test_linear_small(sq, T, O, K):
+    # (20, 700, 512), (32, 300, 256), (1, 256, 128): the 32-row decode tile without a K split;
+    # (48, 700, 512), (64, 256, 256): the 64-row one
     print(f"linear T={T} O={O} K={K}", flush=True)
     p, wc, ws = _random_problem(T, O, K, seed=T * 7 + O)
     y = sq.linear(oracle_prepared(p), w_to_gpu(wc, ws))

@@ -63,3 +63,31 @@ def test_split_k_workspace_shared_across_shapes(sq):
         if seed in seen:
             assert np.array_equal(seen[seed], y)
         seen[seed] = y
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_llama70b_decode_shapes_full_size(sq, T):
+    # the benchmark's decode GEMMs at full size, in the launch configuration it times (split K, 32- and
+    # 64-row decode tiles): gate|up 2 x 28672 x 8192 and down 8192 x 28672, against the oracle on sampled
+    # output columns (weights drawn on the GPU from a fixed seed; the sampled rows are quantised by the oracle)
+    import torch
+    from synth import workload_llama70b_decode
+    print(f"llama70b decode full size T={T}", flush=True)
+    wl = workload_llama70b_decode(T, with_weights=False)
+    H, I = wl["hidden"], wl["inter"]
+    g = torch.Generator(device="cuda").manual_seed(700 + T)
+    for O, K, seed in ((2 * I, H, 1), (H, I, 2)):
+        w_bf = (torch.randn(O, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        wq = sq.quantize_mxfp4(w_bf)
+        rng = np.random.default_rng(seed + T)
+        if K == H:
+            x = wl["x"]
+        else:
+            x = bf16_round((rng.standard_normal((T, K)) * 0.5).astype(np.float32))
+        p = prepare_ref(x, None, 2, 4)
+        y = to_np(sq.linear(oracle_prepared(p), wq))
+        cols = np.unique(np.concatenate([[0, O - 1], rng.choice(O, 96, replace=False)]))
+        w_rows = to_np(w_bf[torch.from_numpy(cols).cuda().long()])
+        wc, ws = quantize_weight_ref(w_rows)
+        y_ref, bound = linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
+        assert_y_close(y[:, cols], y_ref, bound)

@@ -764,13 +764,19 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 // (expert, row-tile) pairs, expert e holding ceil(count_e / BM) row tiles in
 // expert order; the expert is found by a wave-wide prefix sum of the
 // per-expert tile counts. Returns e = -1 (uniform over the workgroup) for the
-// surplus indices of the grid's upper bound.
+// surplus indices of the grid's upper bound. Segment bounds are clamped to
+// [0, P], so malformed offsets never address rows outside the output.
 struct GroupedTile {
   int e;
   TileRows tr;
 };
+__device__ __forceinline__ int64_t seg_bound(const int32_t* __restrict__ seg, int e, int64_t lo, int64_t P) {
+  const int64_t v = seg[e];
+  return v < lo ? lo : v > P ? P : v;
+}
+
 template <class C>
-__device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ seg, int E,
+__device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ seg, int E, int64_t P,
                                                     const int32_t* __restrict__ a_rows) {
   __shared__ int s_info[2];
   const int tid = threadIdx.x;
@@ -781,7 +787,11 @@ __device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ 
     int base = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + tid;
-      const int cnt = e < E ? seg[e + 1] - seg[e] : 0;
+      int cnt = 0;
+      if (e < E) {
+        const int64_t lo = seg_bound(seg, e, 0, P);
+        cnt = (int)(seg_bound(seg, e + 1, lo, P) - lo);
+      }
       const int tiles = (cnt + C::BM - 1) / C::BM;
       const int incl = wave_inclusive_scan(tiles, tid);
       const int excl = incl - tiles;
@@ -796,8 +806,9 @@ __device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ 
   GroupedTile g;
   g.e = s_info[0];
   if (g.e >= 0) {
-    g.tr.m0 = seg[g.e] + (int64_t)s_info[1] * C::BM;
-    const int64_t hi = seg[g.e + 1];
+    const int64_t lo = seg_bound(seg, g.e, 0, P);
+    g.tr.m0 = lo + (int64_t)s_info[1] * C::BM;
+    const int64_t hi = seg_bound(seg, g.e + 1, lo, P);
     g.tr.rows_valid = hi - g.tr.m0 < C::BM ? hi - g.tr.m0 : C::BM;
     g.tr.gather = a_rows;
   }
@@ -816,10 +827,11 @@ __device__ __forceinline__ void select_expert(Operands& op, int e, const uint8_t
 template <bool kRingPath>
 __global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) void linear_grouped_kernel(
     Operands op, const int32_t* __restrict__ a_rows, const int32_t* __restrict__ seg, int E,
-    const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, float* __restrict__ y) {
+    const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, float* __restrict__ y,
+    int64_t P) {
   using C = SmallTile;
   SHARQ_GEMM_LDS(C, kRingPath)
-  const GroupedTile g = grouped_tile<C>(seg, E, a_rows);
+  const GroupedTile g = grouped_tile<C>(seg, E, P, a_rows);
   if (g.e < 0) return;  // uniform across the workgroup
   const int64_t n0 = (int64_t)blockIdx.x * C::BN;
   select_expert(op, g.e, w_codes_all, w_scales_all);
@@ -1008,7 +1020,7 @@ __global__ __launch_bounds__(kThreads, SmallTile::kOccupancy) void linear_groupe
   using C = SmallTile;
   static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
   SHARQ_GEMM_LDS(C, true)
-  const GroupedTile g = grouped_tile<C>(seg, E, a_rows);
+  const GroupedTile g = grouped_tile<C>(seg, E, out.T, a_rows);
   if (g.e < 0) return;
   const int64_t h0 = (int64_t)blockIdx.x * 128;
   select_expert(op, g.e, w_codes_all, w_scales_all);
@@ -1169,10 +1181,10 @@ hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scal
   const dim3 grid(tiles_n, (unsigned)tiles_m_bound);
   if (ring_path_ok(a_rows_total, O, K))
     hipLaunchKernelGGL(linear_grouped_kernel<true>, grid, dim3(kThreads), 0, stream, op, a_rows, seg_offsets, E,
-                       w_codes, w_scales, y);
+                       w_codes, w_scales, y, P);
   else
     hipLaunchKernelGGL(linear_grouped_kernel<false>, grid, dim3(kThreads), 0, stream, op, a_rows, seg_offsets, E,
-                       w_codes, w_scales, y);
+                       w_codes, w_scales, y, P);
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
 // in slot order with one fused multiply-add per slot, so the result does not
 // depend on timing. A lane owns 4 columns of one token row: HBM-bound, k
 // gathered 16-byte reads and one 16-byte (fp32) or 8-byte (bf16) write.
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ y, int64_t H,
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ y, int64_t P, int64_t H,
                                                           const int32_t* __restrict__ pair_index,
                                                           const float* __restrict__ weights, int k,
                                                           uint32_t quads_per_row, uint32_t total,
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
     const int32_t p = pair_index[(int64_t)t * k + j];
-    if (p < 0) continue;
+    if (p < 0 || p >= P) continue;  // empty slot (an index past the pairs is treated as one)
     const float w = weights[(int64_t)t * k + j];
     const float4 v = reinterpret_cast<const float4*>(y + (int64_t)p * H)[c];
     acc.x = fmaf(w, v.x, acc.x);
@@ -67,12 +67,12 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_moe_combine(const float* y, int64_t H, const int32_t* pair_index, const float* weights, int64_t T,
-                              int k, float* out, uint16_t* out_bf16, hipStream_t stream) {
+hipError_t launch_moe_combine(const float* y, int64_t P, int64_t H, const int32_t* pair_index, const float* weights,
+                              int64_t T, int k, float* out, uint16_t* out_bf16, hipStream_t stream) {
   const uint32_t qpr = (uint32_t)(H / 4);
   const uint32_t total = (uint32_t)(T * qpr);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, y, H, pair_index, weights,
-                     k, qpr, total, out, out_bf16);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, y, P, H, pair_index,
+                     weights, k, qpr, total, out, out_bf16);
   return hipGetLastError();
 }
 

@@ -281,7 +281,7 @@ int sharq_moe_combine(const float* y, int64_t P, int64_t H, const int32_t* pair_
   if ((y && !aligned16(y)) || (out && !aligned16(out)) || (out_bf16 && ((uintptr_t)out_bf16 & 7u)) ||
       ((uintptr_t)pair_index & 3u) || ((uintptr_t)weights & 3u))
     return SHARQ_EALIGN;
-  return hip_status(sharq::launch_moe_combine(y, H, pair_index, weights, T, k, out, out_bf16, stream));
+  return hip_status(sharq::launch_moe_combine(y, P, H, pair_index, weights, T, k, out, out_bf16, stream));
 }
 
 int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {

@@ -61,8 +61,8 @@ hipError_t launch_compress_backbone(const uint8_t* bb_codes, const uint8_t* mask
 hipError_t launch_expand_backbone(const uint8_t* codes, const uint8_t* meta, int64_t T, int64_t K, int n, int m,
                                   uint8_t* bb_codes, uint8_t* mask, hipStream_t stream);
 
-hipError_t launch_moe_combine(const float* y, int64_t H, const int32_t* pair_index, const float* weights, int64_t T,
-                              int k, float* out, uint16_t* out_bf16, hipStream_t stream);
+hipError_t launch_moe_combine(const float* y, int64_t P, int64_t H, const int32_t* pair_index, const float* weights,
+                              int64_t T, int k, float* out, uint16_t* out_bf16, hipStream_t stream);
 
 hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream);
 

@@ -185,8 +185,10 @@ SHARQ_API int sharq_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales,
  *  seg_offsets i32 [E+1] device, non-decreasing, [0] = 0, [E] = P.
  *  w_codes u8 [E][G][O][64], w_scales u8 [E][G][O][4] (each expert's
  *              tensor stage-major); y fp32 [P][O].
- * Segment and gather contents are read on the device; their validity is a
- * precondition (a gathered row outside [0, T_src) reads as zeros).
+ * Segment and gather contents are read on the device: segment bounds are
+ * clamped to [0, P] (an empty or reversed segment has no rows), and a
+ * gathered row outside [0, T_src) reads as zeros, so malformed contents give
+ * unspecified values but no access outside the buffers.
  */
 SHARQ_API int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales,
                          const uint8_t* res_codes, const uint8_t* res_scales,
@@ -327,8 +329,8 @@ SHARQ_API int sharq_expand_backbone(const uint8_t* codes, const uint8_t* meta,
  * accumulated in fp32 in slot order j = 0, 1, ... with one fused
  * multiply-add per slot (deterministic).
  *  y           fp32 [P][H], the grouped GEMM's output rows (sorted pairs);
- *  pair_index  i32 [T][k], the pairs of token t (-1: empty slot; each in
- *              [0, P) otherwise, a precondition read on the device);
+ *  pair_index  i32 [T][k], the pairs of token t (-1: empty slot; an index
+ *              outside [0, P) is treated as an empty slot);
  *  weights     fp32 [T][k];
  *  out         fp32 [T][H] or NULL; out_bf16 bf16 [T][H] (the fp32 sum
  *              rounded to nearest even) or NULL; at least one is given.

@@ -184,3 +184,38 @@ def test_moe_combine_small_and_qwen3_size(sq):
     remap = {p: i for i, p in enumerate(np.unique(sub))}
     ref, bound = moe_combine_ref(y_np, np.vectorize(remap.get)(sub).astype(np.int32), w[toks])
     assert np.all(np.abs(out[toks] - ref) <= 2 * k * 2.0 ** -24 * bound + 1e-30)
+
+
+def test_malformed_segments_and_indices_stay_in_bounds(sq):
+    """Device-read routing contents out of range: segment bounds past P or
+    reversed, and combine indices past P. Rows of the output buffer beyond P
+    (guard rows of a larger allocation) must stay untouched, and the valid
+    segments still match the oracle."""
+    import torch
+    from oracle import moe_combine_ref
+    print("grouped malformed segments", flush=True)
+    rng = np.random.default_rng(41)
+    tokens, E, K, O = 200, 4, 256, 256
+    x = bf16_round((rng.standard_normal((tokens, K)) * 2).astype(np.float32))
+    p = prepare_ref(x, None, 2, 4)
+    wc, ws = _experts(E, O, K, rng)
+    P = tokens
+    seg = np.array([0, 60, 140, 120, P + 100], np.int32)  # expert 2 reversed; the last bound past P
+    guard = 256
+    big = torch.full((P + guard, O), 12345.0, dtype=torch.float32, device="cuda")
+    y = sq.linear_grouped(oracle_prepared(p), w_to_gpu(wc, ws), i32_to_gpu(seg), None, out=big[:P])
+    torch.cuda.synchronize()
+    assert torch.all(big[P:] == 12345.0), "rows past P were written"
+    # rows 0 .. 119 belong to experts 0 and 1 only (expert 3's clamped segment [120, P) overlaps expert 1's
+    # tail, whose values are then unspecified): check them against the oracle
+    good = np.array([0, 60, 120], np.int32)
+    y_ref, bound = linear_grouped_ref(p["bb_codes"][:120], p["bb_scales"][:120], p["res_codes"][:120],
+                                      p["res_scales"][:120], None, good, wc[:2], ws[:2])
+    assert_y_close(to_np(y)[:120], y_ref, bound)
+    # combine: an index past P is an empty slot
+    yy = torch.randn(P + guard, 16, device="cuda")
+    idx = np.array([[0, P + 5], [P + guard - 1, 3]], np.int32)
+    w = np.array([[0.5, 2.0], [1.0, 0.25]], np.float32)
+    out = to_np(sq.moe_combine(yy[:P], torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()))
+    ref, bnd = moe_combine_ref(to_np(yy[:P]), np.where(idx < P, idx, -1), w)
+    assert np.all(np.abs(out - ref) <= 4 * 2.0 ** -24 * bnd + 1e-30)

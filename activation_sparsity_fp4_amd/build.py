@@ -15,6 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsharq.so")
 SOURCES = ["prepare.hip", "gemm.hip", "glue.hip", "compact.hip", "sharq_api.hip"]
+CALIB_SOURCE = "calib.hip"
+CALIB_LIB = os.path.join(PKG, "libsharq_calib.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU forms.
@@ -52,8 +54,16 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB)
+    # the benchmark's MFMA-rate calibration kernel, a shared object of its own
+    obj = _compile(CALIB_SOURCE)
+    tmp = CALIB_LIB + ".tmp"
+    res = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 

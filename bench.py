@@ -360,6 +360,34 @@ def copy_rate(torch, n_bytes=1 << 30, reps=10):
     return round(2 * n_bytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
 
 
+def mfma_sustained_rate(torch, reps=5):
+    """TFLOP/s of the scaled FP4 MFMA this GPU sustains on register operands
+    with random bit patterns (no memory traffic; libsharq_calib.so, built
+    beside the library): the rate a GEMM can reach once the power-limited
+    clock is taken into account, reported beside the published peak."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "activation_sparsity_fp4_amd", "libsharq_calib.so"))
+    fn = lib.sharq_calib_mfma_fp4
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(0)
+    blocks, iters = 2 * props.multi_processor_count, 4000
+    out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    flops = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 64
+    ts = []
+    for k in range(reps + 2):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        if fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("MFMA calibration launch failed")
+        b.record()
+        torch.cuda.synchronize()
+        if k >= 2:
+            ts.append(a.elapsed_time(b))
+    return round(flops / (float(np.median(ts)) * 1e-3) / 1e12, 1)
+
+
 def cold_cache_times(stages, steps, torch):
     """Per-stage times with the caches cold: before each step a read of a
     1 GiB buffer evicts L2 and the 256 MB MALL, so every stage reads its
@@ -488,6 +516,12 @@ def main():
         roof = {"kernel": dom.name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "us_per_launch": round(dom_ms * 1e3, 2)}
+    if dom.kind == "mfma" and not args.profile_stage and not args.no_cold:
+        # context: the FP4 MFMA rate this GPU sustains with random operands (power-limited clock), and the
+        # kernel's executed (dense-masked) rate as a fraction of it
+        sustained = mfma_sustained_rate(torch)
+        roof["sustained_mfma_TFLOPs"] = sustained
+        roof["frac_exec_of_sustained"] = round(dom.flops_exec / (dom_ms * 1e-3) / 1e12 / sustained, 4)
     if traffic is not None:
         roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
         roof["algorithmic_bytes"] = round(dom.bytes)

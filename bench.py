@@ -110,10 +110,12 @@ def build_workload(name, torch, sq, unfused=False):
                         prepare_bytes(T, H, True) + 4 * T)] + middle + [
             Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "mfma", gemm_bytes(T, H, I), fa2, fe2),
         ]
+        from synth import array_digest
         cfg = {"workload": "Llama-3.1-8B MLP block, 2048-token prefill, 2:4, MXFP4, RMSNorm (1/rms and gamma) "
                            "absorbed in the first prepare",
                "tokens": T, "hidden": H, "intermediate": I, "nm": "2:4", "rms_eps": eps, "seed": 1002,
-               "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)"}
+               "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)",
+               "input_sha256_16": {k: array_digest(wl[k]) for k in ("x", "gamma", "w_gu", "w_down")}}
 
         def oracle_sample(rows):
             from oracle import linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref

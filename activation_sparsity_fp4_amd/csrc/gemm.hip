@@ -760,14 +760,20 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
   return v;
 }
 
-// Row tile of a grouped launch: blockIdx.y is a linear index over all
-// (expert, row-tile) pairs, expert e holding ceil(count_e / BM) row tiles in
-// expert order; the expert is found by a wave-wide prefix sum of the
+// Tile of a grouped launch. The grid is one-dimensional over (row slot,
+// column tile) pairs, column tiles innermost. With kXcdRanges the pairs are
+// remapped so that each XCD (to which workgroups are dealt round-robin)
+// receives a contiguous range: the column tiles of one row tile then share
+// its activation rows, and the row tiles of one expert its weight tiles, in
+// that XCD's L2. Without it, pair b runs on XCD b mod 8, which for 8 column
+// tiles gives each XCD a fixed column slice of every weight. The row slot is
+// a linear index over all (expert, row-tile) pairs, expert e holding
+// ceil(count_e / BM) row tiles in expert order; the expert is found by a wave-wide prefix sum of the
 // per-expert tile counts. Returns e = -1 (uniform over the workgroup) for the
 // surplus indices of the grid's upper bound. Segment bounds are clamped to
 // [0, P], so malformed offsets never address rows outside the output.
 struct GroupedTile {
-  int e;
+  int e, col;
   TileRows tr;
 };
 __device__ __forceinline__ int64_t seg_bound(const int32_t* __restrict__ seg, int e, int64_t lo, int64_t P) {
@@ -776,23 +782,42 @@ __device__ __forceinline__ int64_t seg_bound(const int32_t* __restrict__ seg, in
 }
 
 template <class C>
+__device__ __forceinline__ int expert_row_tiles(const int32_t* __restrict__ seg, int e, int E, int64_t P) {
+  if (e >= E) return 0;
+  const int64_t lo = seg_bound(seg, e, 0, P);
+  return (int)((seg_bound(seg, e + 1, lo, P) - lo + C::BM - 1) / C::BM);
+}
+
+template <class C, bool kXcdRanges>
 __device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ seg, int E, int64_t P,
-                                                    const int32_t* __restrict__ a_rows) {
-  __shared__ int s_info[2];
+                                                    const int32_t* __restrict__ a_rows, int tiles_n) {
+  __shared__ int s_info[3];
   const int tid = threadIdx.x;
-  const int target = blockIdx.y;
   if (tid == 0) s_info[0] = -1;
   __syncthreads();
   if (tid < 64) {
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + tid;
-      int cnt = 0;
-      if (e < E) {
-        const int64_t lo = seg_bound(seg, e, 0, P);
-        cnt = (int)(seg_bound(seg, e + 1, lo, P) - lo);
+    // With kXcdRanges, pass 1 counts the real tiles A; the first A (rounded
+    // up to 8) workgroups take the work, so that every XCD gets an equal
+    // share, XCD x the logical range [x A8 / 8, (x + 1) A8 / 8).
+    const int b = blockIdx.x;
+    int logical = b, target = b / tiles_n;  // slots past the last tile find no expert
+    if constexpr (kXcdRanges) {
+      int rows_total = 0;
+      for (int e0 = 0; e0 < E; e0 += 64) {
+        int tiles = expert_row_tiles<C>(seg, e0 + tid, E, P);
+        for (int off = 32; off > 0; off >>= 1) tiles += __shfl_xor(tiles, off, 64);
+        rows_total += tiles;
       }
-      const int tiles = (cnt + C::BM - 1) / C::BM;
+      const int A = rows_total * tiles_n, A8 = (A + 7) & ~7;
+      logical = b < A8 ? (b & 7) * (A8 >> 3) + (b >> 3) : A;
+      target = logical < A ? logical / tiles_n : -1;
+    }
+    if (tid == 0) s_info[2] = logical - (logical / tiles_n) * tiles_n;
+    // Pass 2: the expert holding row slot target.
+    int base = 0;
+    for (int e0 = 0; e0 < E && target >= 0; e0 += 64) {
+      const int e = e0 + tid;
+      const int tiles = expert_row_tiles<C>(seg, e, E, P);
       const int incl = wave_inclusive_scan(tiles, tid);
       const int excl = incl - tiles;
       if (e < E && target >= base + excl && target < base + incl) {
@@ -805,6 +830,7 @@ __device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ 
   __syncthreads();
   GroupedTile g;
   g.e = s_info[0];
+  g.col = s_info[2];
   if (g.e >= 0) {
     const int64_t lo = seg_bound(seg, g.e, 0, P);
     g.tr.m0 = lo + (int64_t)s_info[1] * C::BM;
@@ -823,17 +849,17 @@ __device__ __forceinline__ void select_expert(Operands& op, int e, const uint8_t
 }
 
 // Grouped two-path GEMM over token-sorted expert segments (128 x 256 tiles);
-// blockIdx.x is the output column tile, blockIdx.y the (expert, row tile).
+// The grid covers tiles_n column tiles times an upper bound of row slots.
 template <bool kRingPath>
 __global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) void linear_grouped_kernel(
     Operands op, const int32_t* __restrict__ a_rows, const int32_t* __restrict__ seg, int E,
     const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, float* __restrict__ y,
-    int64_t P) {
+    int64_t P, int tiles_n) {
   using C = SmallTile;
   SHARQ_GEMM_LDS(C, kRingPath)
-  const GroupedTile g = grouped_tile<C>(seg, E, P, a_rows);
+  const GroupedTile g = grouped_tile<C, false>(seg, E, P, a_rows, tiles_n);
   if (g.e < 0) return;  // uniform across the workgroup
-  const int64_t n0 = (int64_t)blockIdx.x * C::BN;
+  const int64_t n0 = (int64_t)g.col * C::BN;
   select_expert(op, g.e, w_codes_all, w_scales_all);
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
@@ -1012,17 +1038,17 @@ __global__ __launch_bounds__(256) void split_reduce_silu_prepare_kernel(const fl
 
 // Grouped form of the fused gate|up projection (mixture-of-experts layers):
 // the tile of linear_grouped_kernel's row walk with the fused epilogue;
-// blockIdx.x is the 128-column h tile.
+// the column tile is the 128-column h tile.
 template <int N, int M>
 __global__ __launch_bounds__(kThreads, SmallTile::kOccupancy) void linear_grouped_silu_prepare_kernel(
     Operands op, const int32_t* __restrict__ a_rows, const int32_t* __restrict__ seg, int E,
-    const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, HOutputs out) {
+    const uint8_t* __restrict__ w_codes_all, const uint8_t* __restrict__ w_scales_all, HOutputs out, int tiles_n) {
   using C = SmallTile;
   static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
   SHARQ_GEMM_LDS(C, true)
-  const GroupedTile g = grouped_tile<C>(seg, E, out.T, a_rows);
+  const GroupedTile g = grouped_tile<C, true>(seg, E, out.T, a_rows, tiles_n);
   if (g.e < 0) return;
-  const int64_t h0 = (int64_t)blockIdx.x * 128;
+  const int64_t h0 = (int64_t)g.col * 128;
   select_expert(op, g.e, w_codes_all, w_scales_all);
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
@@ -1178,13 +1204,14 @@ hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scal
   // every expert contributes ceil(count / 128) row tiles: at most P/128 + E in total
   const int64_t tiles_m_bound = (P + SmallTile::BM - 1) / SmallTile::BM + E;
   const int tiles_n = (int)((O + SmallTile::BN - 1) / SmallTile::BN);
-  const dim3 grid(tiles_n, (unsigned)tiles_m_bound);
+  const int total = (int)(tiles_n * tiles_m_bound);
+  const dim3 grid((unsigned)total);
   if (ring_path_ok(a_rows_total, O, K))
     hipLaunchKernelGGL(linear_grouped_kernel<true>, grid, dim3(kThreads), 0, stream, op, a_rows, seg_offsets, E,
-                       w_codes, w_scales, y, P);
+                       w_codes, w_scales, y, P, tiles_n);
   else
     hipLaunchKernelGGL(linear_grouped_kernel<false>, grid, dim3(kThreads), 0, stream, op, a_rows, seg_offsets, E,
-                       w_codes, w_scales, y, P);
+                       w_codes, w_scales, y, P, tiles_n);
   return hipGetLastError();
 }
 
@@ -1246,13 +1273,15 @@ hipError_t launch_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uin
       make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, a_rows_total, 2 * I, K);
   const HOutputs out{h, h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, P, I};
   const int64_t tiles_m_bound = (P + SmallTile::BM - 1) / SmallTile::BM + E;
-  const dim3 grid((unsigned)(I / 128), (unsigned)tiles_m_bound);
+  const int tiles_n = (int)(I / 128);
+  const int total = (int)(tiles_n * tiles_m_bound);
+  const dim3 grid((unsigned)total);
   if (n == 2 && m == 4)
     hipLaunchKernelGGL((linear_grouped_silu_prepare_kernel<2, 4>), grid, dim3(kThreads), 0, stream, op, a_rows,
-                       seg_offsets, E, w_codes, w_scales, out);
+                       seg_offsets, E, w_codes, w_scales, out, tiles_n);
   else
     hipLaunchKernelGGL((linear_grouped_silu_prepare_kernel<8, 16>), grid, dim3(kThreads), 0, stream, op, a_rows,
-                       seg_offsets, E, w_codes, w_scales, out);
+                       seg_offsets, E, w_codes, w_scales, out, tiles_n);
   return hipGetLastError();
 }
 

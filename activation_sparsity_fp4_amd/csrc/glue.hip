@@ -37,6 +37,24 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
 // in slot order with one fused multiply-add per slot, so the result does not
 // depend on timing. A lane owns 4 columns of one token row: HBM-bound, k
 // gathered 16-byte reads and one 16-byte (fp32) or 8-byte (bf16) write.
+__device__ __forceinline__ void combine_store(float4 acc, int64_t t, uint32_t c, int64_t H, float* __restrict__ out,
+                                              uint16_t* __restrict__ out_bf16) {
+  if (out) reinterpret_cast<float4*>(out + t * H)[c] = acc;
+  if (out_bf16) {
+    const uint32_t lo = bf16_rne_bits(acc.x) | (bf16_rne_bits(acc.y) << 16);
+    const uint32_t hi = bf16_rne_bits(acc.z) | (bf16_rne_bits(acc.w) << 16);
+    reinterpret_cast<uint2*>(out_bf16 + t * H)[c] = make_uint2(lo, hi);
+  }
+}
+
+__device__ __forceinline__ void combine_fma(float4& acc, float w, float4 v) {
+  acc.x = fmaf(w, v.x, acc.x);
+  acc.y = fmaf(w, v.y, acc.y);
+  acc.z = fmaf(w, v.z, acc.z);
+  acc.w = fmaf(w, v.w, acc.w);
+}
+
+// Any k: slot by slot.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ y, int64_t P, int64_t H,
                                                           const int32_t* __restrict__ pair_index,
                                                           const float* __restrict__ weights, int k,
@@ -50,19 +68,48 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   for (int j = 0; j < k; ++j) {
     const int32_t p = pair_index[(int64_t)t * k + j];
     if (p < 0 || p >= P) continue;  // empty slot (an index past the pairs is treated as one)
-    const float w = weights[(int64_t)t * k + j];
-    const float4 v = reinterpret_cast<const float4*>(y + (int64_t)p * H)[c];
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
+    combine_fma(acc, weights[(int64_t)t * k + j], reinterpret_cast<const float4*>(y + (int64_t)p * H)[c]);
   }
-  if (out) reinterpret_cast<float4*>(out + (int64_t)t * H)[c] = acc;
-  if (out_bf16) {
-    const uint32_t lo = bf16_rne_bits(acc.x) | (bf16_rne_bits(acc.y) << 16);
-    const uint32_t hi = bf16_rne_bits(acc.z) | (bf16_rne_bits(acc.w) << 16);
-    reinterpret_cast<uint2*>(out_bf16 + (int64_t)t * H)[c] = make_uint2(lo, hi);
+  combine_store(acc, t, c, H, out, out_bf16);
+}
+
+// k == K, a compile-time constant (and P > 0): all slot indices and weights
+// are loaded first, then all K row reads are issued before the first is used,
+// so a lane keeps K reads in flight instead of one. Empty slots read row 0 (in
+// bounds) and are then left out by a select; the sum is the same slot-order
+// chain of FMAs.
+template <int K>
+__global__ __launch_bounds__(256) void moe_combine_batched_kernel(const float* __restrict__ y, int64_t P, int64_t H,
+                                                                  const int32_t* __restrict__ pair_index,
+                                                                  const float* __restrict__ weights,
+                                                                  uint32_t quads_per_row, uint32_t total,
+                                                                  float* __restrict__ out,
+                                                                  uint16_t* __restrict__ out_bf16) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= total) return;
+  const uint32_t t = gid / quads_per_row;
+  const uint32_t c = gid - t * quads_per_row;
+  int32_t p[K];
+  float w[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    p[j] = pair_index[(int64_t)t * K + j];
+    w[j] = weights[(int64_t)t * K + j];
   }
+  float4 v[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const bool ok = p[j] >= 0 && p[j] < P;
+    v[j] = reinterpret_cast<const float4*>(y + (int64_t)(ok ? p[j] : 0) * H)[c];
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    float4 next = acc;
+    combine_fma(next, w[j], v[j]);
+    if (p[j] >= 0 && p[j] < P) acc = next;
+  }
+  combine_store(acc, t, c, H, out, out_bf16);
 }
 
 }  // namespace
@@ -71,8 +118,19 @@ hipError_t launch_moe_combine(const float* y, int64_t P, int64_t H, const int32_
                               int64_t T, int k, float* out, uint16_t* out_bf16, hipStream_t stream) {
   const uint32_t qpr = (uint32_t)(H / 4);
   const uint32_t total = (uint32_t)(T * qpr);
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((total + 255) / 256), dim3(256), 0, stream, y, P, H, pair_index,
-                     weights, k, qpr, total, out, out_bf16);
+  const dim3 grid((total + 255) / 256);
+  if (P > 0 && k == 8)
+    hipLaunchKernelGGL(moe_combine_batched_kernel<8>, grid, dim3(256), 0, stream, y, P, H, pair_index, weights, qpr,
+                       total, out, out_bf16);
+  else if (P > 0 && k == 4)
+    hipLaunchKernelGGL(moe_combine_batched_kernel<4>, grid, dim3(256), 0, stream, y, P, H, pair_index, weights, qpr,
+                       total, out, out_bf16);
+  else if (P > 0 && k == 2)
+    hipLaunchKernelGGL(moe_combine_batched_kernel<2>, grid, dim3(256), 0, stream, y, P, H, pair_index, weights, qpr,
+                       total, out, out_bf16);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel, grid, dim3(256), 0, stream, y, P, H, pair_index, weights, k, qpr, total,
+                       out, out_bf16);
   return hipGetLastError();
 }
 

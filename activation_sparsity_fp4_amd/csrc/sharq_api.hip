@@ -9,6 +9,9 @@
 namespace {
 
 constexpr int kAbiVersion = 6;
+// Workgroups of one grouped launch: a one-dimensional grid of 256-thread
+// workgroups whose thread count must stay below 2^32.
+constexpr int64_t kMaxGroupedTiles = (int64_t)1 << 24;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -169,7 +172,7 @@ int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales, cons
   if (!a_rows && T_src < P) return SHARQ_EINVAL;
   if (T_src >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
   if (P >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31) ||
-      (P + 127) / 128 + E > 65535)
+      ((P + 127) / 128 + E) * ((O + 255) / 256) > kMaxGroupedTiles)
     return SHARQ_EINVAL;
   if (P == 0 || O == 0) return SHARQ_OK;
   if (!bb_codes || !bb_scales || !res_codes || !res_scales || !seg_offsets || !w_codes || !w_scales || !y)
@@ -222,7 +225,7 @@ int sharq_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb
   if (E < 1 || P < 0 || I <= 0 || K <= 0 || K % 32 != 0 || I % 32 != 0 || T_src < 0) return SHARQ_EINVAL;
   if (!a_rows && T_src < P) return SHARQ_EINVAL;
   if (T_src >= ((int64_t)1 << 31) || P >= ((int64_t)1 << 31) || I >= ((int64_t)1 << 30) ||
-      K >= ((int64_t)1 << 31) || (P + 127) / 128 + E > 65535)
+      K >= ((int64_t)1 << 31) || ((P + 127) / 128 + E) * (I / 128) > kMaxGroupedTiles)
     return SHARQ_EINVAL;
   if (P * (I / 32) >= ((int64_t)1 << 31)) return SHARQ_EINVAL;  // 32-bit block index of the h blocks
   if (I % 128 != 0 || K % 128 != 0) return SHARQ_ENOTIMPL;     // whole 128-column h tiles, ring path only

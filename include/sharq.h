@@ -189,6 +189,8 @@ SHARQ_API int sharq_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales,
  * clamped to [0, P] (an empty or reversed segment has no rows), and a
  * gathered row outside [0, T_src) reads as zeros, so malformed contents give
  * unspecified values but no access outside the buffers.
+ * SHARQ_EINVAL also when (ceil(P/128) + E) * ceil(O/256), the bound on the
+ * number of 128 x 256 tiles, exceeds 2^24.
  */
 SHARQ_API int sharq_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales,
                          const uint8_t* res_codes, const uint8_t* res_scales,
@@ -267,7 +269,8 @@ SHARQ_API int sharq_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_
  *              with pattern n:m, or all four NULL (then h must be given).
  * Outputs are bit-identical to sharq_linear_grouped + sharq_silu_mul +
  * sharq_prepare. Requires I % 128 == 0 and K % 128 == 0 (SHARQ_ENOTIMPL
- * otherwise), T_src * K / 2 < 2^31 and I * K < 2^31 (SHARQ_ENOTIMPL).
+ * otherwise), T_src * K / 2 < 2^31 and I * K < 2^31 (SHARQ_ENOTIMPL);
+ * SHARQ_EINVAL when (ceil(P/128) + E) * I / 128 exceeds 2^24.
  */
 SHARQ_API int sharq_linear_grouped_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales,
                               const uint8_t* res_codes, const uint8_t* res_scales,

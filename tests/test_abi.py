@@ -104,7 +104,8 @@ def test_grouped_validation():
     assert grp(seg=0) == _lib.SHARQ_EINVAL
     assert grp(K=40) == _lib.SHARQ_EINVAL
     assert grp(a_rows=A + 4) == _lib.SHARQ_EALIGN
-    assert grp(P=1 << 24, E=1) == _lib.SHARQ_EINVAL  # grid bound
+    assert grp(P=1 << 24, E=1, O=1 << 16) == _lib.SHARQ_EINVAL  # grid bound: over 2^24 tiles
+    assert grp(P=128, E=1 << 20, O=1 << 13) == _lib.SHARQ_EINVAL  # grid bound from the experts
     assert grp(a_rows=0, T_src=8) == _lib.SHARQ_EINVAL  # identity rows need T_src >= P
     assert grp(T_src=-1) == _lib.SHARQ_EINVAL
 
@@ -218,7 +219,8 @@ def test_linear_grouped_silu_prepare_validation():
     assert gfused(K=96) == _lib.SHARQ_ENOTIMPL
     assert gfused(I=96) == _lib.SHARQ_ENOTIMPL
     assert gfused(I=100) == _lib.SHARQ_EINVAL
-    assert gfused(P=1 << 24, E=1, T_src=1 << 24) == _lib.SHARQ_EINVAL    # grid bound
+    assert gfused(P=1 << 24, E=1, T_src=1 << 24, I=1 << 12) == _lib.SHARQ_EINVAL  # h block index bound
+    assert gfused(P=128, E=1 << 20, I=1 << 12) == _lib.SHARQ_EINVAL      # grid bound: over 2^24 tiles
     assert gfused(a_rows=A + 4) == _lib.SHARQ_EALIGN
     assert gfused(h=G + 2) == _lib.SHARQ_EALIGN
     assert gfused(T_src=1 << 20, K=1 << 12, P=8) == _lib.SHARQ_ENOTIMPL  # activation codes past 32-bit offsets

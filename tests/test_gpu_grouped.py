@@ -162,14 +162,15 @@ def test_moe_combine_small_and_qwen3_size(sq):
     print("moe combine small", flush=True)
     rng = np.random.default_rng(14)
     y = (rng.standard_normal((60, 32)) * rng.lognormal(0, 2, (60, 1))).astype(np.float32)
-    idx = rng.integers(-1, 60, (23, 5)).astype(np.int32)
-    w = rng.uniform(-1, 1, (23, 5)).astype(np.float32)
     yg = torch.from_numpy(y).cuda()
-    out = to_np(sq.moe_combine(yg, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()))
-    ref, bound = moe_combine_ref(y, idx, w)
-    assert np.all(np.abs(out - ref) <= 2 * 5 * 2.0 ** -24 * bound + 1e-30)
-    outb = to_np(sq.moe_combine(yg, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), bf16=True))
-    assert np.array_equal(outb, f32_to_bf16_bits_rne(out))
+    for k in (1, 2, 4, 5, 8, 9):  # the k = 2, 4, 8 kernels and the general one
+        idx = rng.integers(-1, 60, (23, k)).astype(np.int32)
+        w = rng.uniform(-1, 1, (23, k)).astype(np.float32)
+        out = to_np(sq.moe_combine(yg, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()))
+        ref, bound = moe_combine_ref(y, idx, w)
+        assert np.all(np.abs(out - ref) <= 2 * k * 2.0 ** -24 * bound + 1e-30), k
+        outb = to_np(sq.moe_combine(yg, torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), bf16=True))
+        assert np.array_equal(outb, f32_to_bf16_bits_rne(out)), k
     # the Qwen3-30B-A3B layer: 4096 tokens x top-8 over 32768 sorted pairs, H = 2048
     print("moe combine qwen3 size", flush=True)
     wl = workload_qwen3_moe(with_weights=False)

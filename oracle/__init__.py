@@ -7,3 +7,4 @@ It shares no code with the HIP library under ``activation_sparsity_fp4_amd``.
 
 from .sharq_ref import *  # noqa: F401,F403
 from .compact_ref import *  # noqa: F401,F403
+from .nvfp4_ref import *  # noqa: F401,F403

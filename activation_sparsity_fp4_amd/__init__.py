@@ -31,6 +31,11 @@ __all__ = [
     "expand_backbone",
     "moe_combine",
     "silu_mul",
+    "NVPrepared",
+    "NVFP4",
+    "prepare_nvfp4",
+    "quantize_nvfp4",
+    "linear_nvfp4",
     "SharqError",
     "status_string",
 ]
@@ -443,4 +448,110 @@ def silu_mul(gu, out=None):
         out = torch.empty((T, I), dtype=torch.bfloat16, device=gu.device)
     st = _lib.call("sharq_silu_mul", gu.data_ptr(), T, I, out.data_ptr(), _stream(gu.device))
     _lib.check("sharq_silu_mul", st)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# NVFP4: 16-entry E2M1 blocks with E4M3 block scales and an fp32 tensor scale
+# ---------------------------------------------------------------------------
+
+
+class NVPrepared(NamedTuple):
+    """Outputs of the NVFP4 prepare: codes [G, T, 64] as in Prepared, E4M3
+    block scales [G, T, 8] (byte j of a row's stage g covers K entries
+    128 g + 16 j .. + 15), the mask, K and the activation's tensor scale."""
+    bb_codes: "object"
+    bb_scales: "object"
+    res_codes: "object"
+    res_scales: "object"
+    mask: "object"
+    K: int
+    tensor_scale: float
+
+
+class NVFP4(NamedTuple):
+    """An NVFP4 tensor, stage-major: codes [G, R, 64], E4M3 scales [G, R, 8]."""
+    codes: "object"
+    scales: "object"
+    K: int
+    tensor_scale: float
+
+
+def _check_nv(codes, scales, R, K, name):
+    torch = _torch()
+    _need(codes, torch.uint8, name + ".codes", 3)
+    _need(scales, torch.uint8, name + ".scales", 3)
+    G = stages(K)
+    if tuple(codes.shape) != (G, R, 64) or tuple(scales.shape) != (G, R, 8):
+        raise ValueError(f"{name}: expected codes [{G}, {R}, 64] and scales [{G}, {R}, 8], "
+                         f"got {tuple(codes.shape)} and {tuple(scales.shape)}")
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError(f"{name}: codes and scales must be contiguous")
+
+
+def prepare_nvfp4(x, tensor_scale: float, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True,
+                  out: Optional[NVPrepared] = None) -> NVPrepared:
+    """The prepare operator with NVFP4 codes; tensor_scale is the activation's
+    fp32 tensor scale (shared by backbone and residual)."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x", 2)
+    if x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous along K")
+    T, K = x.shape
+    if gamma is not None:
+        _need(gamma, torch.bfloat16, "gamma", 1)
+        gamma = gamma.contiguous()
+    if out is None:
+        kw = dict(dtype=torch.uint8, device=x.device)
+        G = stages(K)
+        out = NVPrepared(torch.empty((G, T, 64), **kw), torch.empty((G, T, 8), **kw),
+                         torch.empty((G, T, 64), **kw), torch.empty((G, T, 8), **kw),
+                         torch.empty((T, K // 8), **kw) if with_mask else None, K, float(tensor_scale))
+    elif out.K != K:
+        raise ValueError("out was allocated for another K")
+    else:
+        out = out._replace(tensor_scale=float(tensor_scale))
+    st = _lib.call("sharq_prepare_nvfp4", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), n, m, float(tensor_scale),
+                   out.bb_codes.data_ptr(), out.bb_scales.data_ptr(), out.res_codes.data_ptr(),
+                   out.res_scales.data_ptr(), _ptr(out.mask), _stream(x.device))
+    _lib.check("sharq_prepare_nvfp4", st)
+    return out
+
+
+def quantize_nvfp4(w, tensor_scale: float, out: Optional[NVFP4] = None) -> NVFP4:
+    """NVFP4 of a bf16 [O, K] tensor with the given fp32 tensor scale."""
+    torch = _torch()
+    _need(w, torch.bfloat16, "w", 2)
+    if w.stride(1) != 1:
+        raise ValueError("w rows must be contiguous along K")
+    O, K = w.shape
+    if out is None:
+        out = NVFP4(torch.empty((stages(K), O, 64), dtype=torch.uint8, device=w.device),
+                    torch.empty((stages(K), O, 8), dtype=torch.uint8, device=w.device), K, float(tensor_scale))
+    else:
+        out = out._replace(tensor_scale=float(tensor_scale))
+    st = _lib.call("sharq_quantize_nvfp4", w.data_ptr(), O, K, w.stride(0), float(tensor_scale),
+                   out.codes.data_ptr(), out.scales.data_ptr(), _stream(w.device))
+    _lib.check("sharq_quantize_nvfp4", st)
+    return out
+
+
+def linear_nvfp4(prep: NVPrepared, w: NVFP4, out=None):
+    """Two-path GEMM on NVFP4 operands: Y = deq(A_s) W^T + deq(A_r) W^T, fp32 [T, O]."""
+    torch = _torch()
+    T, K = prep.bb_codes.shape[1], prep.K
+    O = w.codes.shape[1]
+    _check_nv(prep.bb_codes, prep.bb_scales, T, K, "backbone")
+    _check_nv(prep.res_codes, prep.res_scales, T, K, "residual")
+    _check_nv(w.codes, w.scales, O, K, "w")
+    if w.K != K:
+        raise ValueError("weight K does not match the activation K")
+    if out is None:
+        out = torch.empty((T, O), dtype=torch.float32, device=prep.bb_codes.device)
+    _need(out, torch.float32, "out", 2)
+    st = _lib.call("sharq_linear_nvfp4", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
+                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), float(prep.tensor_scale),
+                   w.codes.data_ptr(), w.scales.data_ptr(), float(w.tensor_scale), T, O, K, out.data_ptr(),
+                   out.stride(0), _stream(out.device))
+    _lib.check("sharq_linear_nvfp4", st)
     return out

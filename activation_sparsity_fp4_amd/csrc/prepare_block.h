@@ -102,34 +102,38 @@ __device__ __forceinline__ uint32_t select_exact(const float (&x)[32]) {
   return mask;
 }
 
+// N:M mask bits of one 32-entry block and its backbone xs (kept entries,
+// zeros elsewhere). kMaybeLowBits: x' may have non-zero low key bits
+// (x * gamma), so the block checks and takes the exact selection when needed.
+template <int N, int M, bool kMaybeLowBits>
+__device__ __forceinline__ uint32_t select_block(const float (&xv)[32], float (&xs)[32]) {
+  if constexpr (kMaybeLowBits) {
+    uint32_t low = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) low |= __float_as_uint(xv[k]);
+    if (low & (uint32_t)(M - 1)) {
+      const uint32_t keep = select_exact<N, M>(xv);
+#pragma unroll
+      for (int k = 0; k < 32; ++k) xs[k] = (keep >> k) & 1u ? xv[k] : 0.0f;
+      return keep;
+    }
+  }
+  return select_fast<N, M>(xv, xs);
+}
+
 struct PreparedBlock {
   uint4 c_bb, c_rs;      // backbone and residual E2M1 codes (16 bytes each)
   uint32_t e_bb, e_rs;   // E8M0 scale bytes
   uint32_t keep;         // mask bits, bit k for entry k
 };
 
-// One block. kMaybeLowBits: x' may have non-zero low key bits (x * gamma), so
-// each block checks and takes the exact selection path when needed.
+// One block (kMaybeLowBits as for select_block).
 template <int N, int M, bool kMaybeLowBits>
 __device__ __forceinline__ PreparedBlock prepare_block(const float (&xv)[32]) {
   PreparedBlock out;
   // N:M selection; xs = the backbone (kept entries, zeros elsewhere)
-  uint32_t keep;
   float xs[32];
-  if constexpr (kMaybeLowBits) {
-    uint32_t low = 0;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) low |= __float_as_uint(xv[k]);
-    if (low & (uint32_t)(M - 1)) {
-      keep = select_exact<N, M>(xv);
-#pragma unroll
-      for (int k = 0; k < 32; ++k) xs[k] = (keep >> k) & 1u ? xv[k] : 0.0f;
-    } else {
-      keep = select_fast<N, M>(xv, xs);
-    }
-  } else {
-    keep = select_fast<N, M>(xv, xs);
-  }
+  const uint32_t keep = select_block<N, M, kMaybeLowBits>(xv, xs);
 
   // backbone: the block's largest |x'| is always kept (each group keeps its
   // maximum), so the backbone scale is the block's plain MX scale

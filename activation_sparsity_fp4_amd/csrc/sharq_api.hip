@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 // Workgroups of one grouped launch: a one-dimensional grid of 256-thread
 // workgroups whose thread count must stay below 2^32.
 constexpr int64_t kMaxGroupedTiles = (int64_t)1 << 24;
@@ -128,6 +128,52 @@ int sharq_quantize_mxfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, u
   if (!x || !codes || !scales) return SHARQ_EINVAL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return SHARQ_EALIGN;
   return hip_status(sharq::launch_quantize(x, T, K, ldx, codes, scales, stream));
+}
+
+int sharq_prepare_nvfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma, int n, int m,
+                        float tensor_scale, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
+                        uint8_t* res_scales, uint8_t* mask, hipStream_t stream) {
+  if (!((n == 2 && m == 4) || (n == 8 && m == 16))) return SHARQ_EUNSUPPORTED;
+  const int rc = check_rows(T, K, ldx);
+  if (rc != SHARQ_OK) return rc;
+  if (K % m != 0 || !(tensor_scale > 0.0f) || !(tensor_scale < INFINITY)) return SHARQ_EINVAL;
+  if (T == 0) return SHARQ_OK;
+  if (!x || !bb_codes || !bb_scales || !res_codes || !res_scales) return SHARQ_EINVAL;
+  if (!aligned16(x) || (gamma && !aligned16(gamma)) || !aligned16(bb_codes) || !aligned16(bb_scales) ||
+      !aligned16(res_codes) || !aligned16(res_scales) || (mask && !aligned16(mask)))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_prepare_nvfp4(x, T, K, ldx, gamma, n, m, tensor_scale, bb_codes, bb_scales,
+                                                res_codes, res_scales, mask, stream));
+}
+
+int sharq_quantize_nvfp4(const uint16_t* w, int64_t O, int64_t K, int64_t ldw, float tensor_scale, uint8_t* codes,
+                         uint8_t* scales, hipStream_t stream) {
+  const int rc = check_rows(O, K, ldw);
+  if (rc != SHARQ_OK) return rc;
+  if (!(tensor_scale > 0.0f) || !(tensor_scale < INFINITY)) return SHARQ_EINVAL;
+  if (O == 0) return SHARQ_OK;
+  if (!w || !codes || !scales) return SHARQ_EINVAL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_quantize_nvfp4(w, O, K, ldw, tensor_scale, codes, scales, stream));
+}
+
+int sharq_linear_nvfp4(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                       const uint8_t* res_scales, float a_tensor_scale, const uint8_t* w_codes,
+                       const uint8_t* w_scales, float w_tensor_scale, int64_t T, int64_t O, int64_t K, float* y,
+                       int64_t ldy, hipStream_t stream) {
+  if (T < 0 || O < 0 || K <= 0 || K % 32 != 0 || ldy < O) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (!(a_tensor_scale > 0.0f) || !(a_tensor_scale < INFINITY) || !(w_tensor_scale > 0.0f) ||
+      !(w_tensor_scale < INFINITY))
+    return SHARQ_EINVAL;
+  if (((T + 127) / 128) * ((O + 255) / 256) > ((int64_t)1 << 24)) return SHARQ_EINVAL;  // one-dimensional grid
+  if (T == 0 || O == 0) return SHARQ_OK;
+  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !w_codes || !w_scales || !y) return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
+      !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y))
+    return SHARQ_EALIGN;
+  return hip_status(sharq::launch_linear_nvfp4(bb_codes, bb_scales, res_codes, res_scales, a_tensor_scale, w_codes,
+                                               w_scales, w_tensor_scale, T, O, K, y, ldy, stream));
 }
 
 int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,

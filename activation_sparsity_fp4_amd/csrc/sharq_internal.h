@@ -64,6 +64,18 @@ hipError_t launch_expand_backbone(const uint8_t* codes, const uint8_t* meta, int
 hipError_t launch_moe_combine(const float* y, int64_t P, int64_t H, const int32_t* pair_index, const float* weights,
                               int64_t T, int k, float* out, uint16_t* out_bf16, hipStream_t stream);
 
+hipError_t launch_prepare_nvfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx, const uint16_t* gamma, int n,
+                                int m, float s_t, uint8_t* bb_codes, uint8_t* bb_scales, uint8_t* res_codes,
+                                uint8_t* res_scales, uint8_t* mask, hipStream_t stream);
+
+hipError_t launch_quantize_nvfp4(const uint16_t* w, int64_t O, int64_t K, int64_t ldw, float s_t, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_linear_nvfp4(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                               const uint8_t* res_scales, float s_a, const uint8_t* w_codes, const uint8_t* w_scales,
+                               float s_w, int64_t T, int64_t O, int64_t K, float* y, int64_t ldy,
+                               hipStream_t stream);
+
 hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream);
 
 }  // namespace sharq

@@ -30,10 +30,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 scaled MFMA
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 MFMA (the NVFP4 GEMM widens its codes to fp16)
 
 WORKLOADS = ["llama8b_mlp", "linear_128x4096", "down_8of16", "down_2of4", "llama70b_decode_T1",
              "llama70b_decode_T8", "llama70b_decode_T32", "llama70b_decode_T64", "qwen3_moe", "compact_2of4",
-             "compact_8of16"]
+             "compact_8of16", "nvfp4_down_8of16", "nvfp4_down_2of4"]
 
 
 def prepare_bytes(T, K, gamma=False):
@@ -66,10 +67,22 @@ def _to_gpu_bf16(torch, u16):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def nv_prepare_bytes(T, K):
+    """NVFP4 prepare: read bf16 x, write two code arrays (0.5/elem each), two E4M3
+    scale arrays (1/16 each) and the mask (1/8)."""
+    return T * K * (2 + 0.5 + 0.5 + 2 / 16 + 1 / 8)
+
+
+def nv_gemm_bytes(T, O, K):
+    """Minimum HBM bytes of the NVFP4 two-path GEMM: both A operands, W once, fp32 Y."""
+    return 2 * T * K * 9 / 16 + O * K * 9 / 16 + 4 * T * O
+
+
 class Stage:
-    def __init__(self, name, fn, kind, bytes_=0.0, flops_alg=0.0, flops_exec=0.0):
+    def __init__(self, name, fn, kind, bytes_=0.0, flops_alg=0.0, flops_exec=0.0, peak=FP4_PEAK_TFLOPS):
         self.name, self.fn, self.kind = name, fn, kind
         self.bytes, self.flops_alg, self.flops_exec = bytes_, flops_alg, flops_exec
+        self.peak = peak  # TFLOP/s of the matrix unit the stage runs on
 
 
 def build_workload(name, torch, sq, unfused=False):
@@ -158,6 +171,39 @@ def build_workload(name, torch, sq, unfused=False):
             p = prepare_ref(xb[:rows], None, n, m)
             wc, ws = quantize_weight_ref(wb)
             linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
+            return time.perf_counter() - t0
+        return stages, T, cfg, oracle_sample
+
+    if name.startswith("nvfp4_down_"):
+        # the down projection with NVFP4 operands (16-entry blocks, E4M3 block scales, fp32 tensor scales)
+        from synth import bf16_to_f32
+        wl = workload_down_silu()
+        xb, wb = wl["x"], wl["w"]
+        n, m = (8, 16) if name == "nvfp4_down_8of16" else (2, 4)
+        T, K = xb.shape
+        O = wb.shape[0]
+        # static tensor scales amax / (6 * 448), calibrated on the host from the same data
+        s_a = float(np.float32(np.abs(bf16_to_f32(xb)).max()) / np.float32(2688.0))
+        s_w = float(np.float32(np.abs(bf16_to_f32(wb)).max()) / np.float32(2688.0))
+        x = _to_gpu_bf16(torch, xb)
+        wq = sq.quantize_nvfp4(_to_gpu_bf16(torch, wb), s_w)
+        buf = {"p": sq.prepare_nvfp4(x, s_a, None, n, m)}
+        buf["y"] = sq.linear_nvfp4(buf["p"], wq)
+        fa, fe = gemm_flops(T, O, K, n, m)
+        stages = [Stage("prepare_nvfp4", lambda: sq.prepare_nvfp4(x, s_a, None, n, m, out=buf["p"]), "hbm",
+                        nv_prepare_bytes(T, K)),
+                  Stage("gemm_nvfp4", lambda: sq.linear_nvfp4(buf["p"], wq, out=buf["y"]), "mfma",
+                        nv_gemm_bytes(T, O, K), fa, fe, F16_PEAK_TFLOPS)]
+        cfg = {"workload": f"down_proj 2048x14336 -> 4096, {n}:{m}, NVFP4 (GEMM on fp16 MFMA), SiLU-gated input",
+               "tokens": T, "in_features": K, "out_features": O, "nm": f"{n}:{m}", "format": "nvfp4",
+               "tensor_scales": {"activation": s_a, "weight": s_w}}
+
+        def oracle_sample(rows):
+            from oracle import linear_nvfp4_ref, prepare_nvfp4_ref, quantize_weight_nvfp4_ref
+            t0 = time.perf_counter()
+            p = prepare_nvfp4_ref(xb[:rows], None, n, m, s_a)
+            wc, ws = quantize_weight_nvfp4_ref(wb, s_w)
+            linear_nvfp4_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], s_a, wc, ws, s_w)
             return time.perf_counter() - t0
         return stages, T, cfg, oracle_sample
 
@@ -279,15 +325,15 @@ def build_workload(name, torch, sq, unfused=False):
 
 
 KERNEL_SOURCES = {"gemm": ["gemm.hip"], "prepare": ["prepare.hip"], "silu": ["glue.hip", "silu.h"],
-                  "grouped": ["gemm.hip"], "compact": ["compact.hip"]}
-SHARED_HEADERS = ["sharq_device.h", "prepare_block.h", "sort_network.h", "silu.h"]
+                  "grouped": ["gemm.hip"], "compact": ["compact.hip"], "nvfp4": ["nvfp4.hip"]}
+SHARED_HEADERS = ["sharq_device.h", "prepare_block.h", "prepare_io.h", "sort_network.h", "silu.h"]
 
 
 def source_digest(stage_name):
     """sha256 over the HIP sources that implement a stage and the device headers
     they include (ties recorded counters to a kernel version)."""
     import hashlib
-    key = "gemm" if "gemm" in stage_name or "grouped" in stage_name else (
+    key = "nvfp4" if "nvfp4" in stage_name else "gemm" if "gemm" in stage_name or "grouped" in stage_name else (
         "silu" if "silu" in stage_name else "compact" if "backbone" in stage_name else "prepare")
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[key] + SHARED_HEADERS:
@@ -501,7 +547,7 @@ def main():
         if s.flops_alg:
             d["TFLOP/s_alg"] = round(s.flops_alg / (ms * 1e-3) / 1e12, 1)
             d["TFLOP/s_exec"] = round(s.flops_exec / (ms * 1e-3) / 1e12, 1)
-            d["mfma_frac_alg"] = round(d["TFLOP/s_alg"] / FP4_PEAK_TFLOPS, 4)
+            d["mfma_frac_alg"] = round(d["TFLOP/s_alg"] / s.peak, 4)
         breakdown[s.name] = d
 
     # dominant kernel: the stage with the largest median duration in the breakdown;
@@ -510,15 +556,15 @@ def main():
     traffic = recorded_traffic(args.workload, dom.name)
     if dom.kind == "mfma":
         ach = dom.flops_alg / (dom_ms * 1e-3) / 1e12
-        roof = {"kernel": dom.name, "bound": "mfma", "achieved": round(ach, 1), "peak": FP4_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / FP4_PEAK_TFLOPS, 4), "traffic": traffic,
+        roof = {"kernel": dom.name, "bound": "mfma", "achieved": round(ach, 1), "peak": dom.peak,
+                "unit": "TFLOP/s", "frac": round(ach / dom.peak, 4), "traffic": traffic,
                 "us_per_launch": round(dom_ms * 1e3, 2)}
     else:
         ach = dom.bytes / (dom_ms * 1e-3) / 1e9
         roof = {"kernel": dom.name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "us_per_launch": round(dom_ms * 1e3, 2)}
-    if dom.kind == "mfma" and not args.profile_stage and not args.no_cold:
+    if dom.kind == "mfma" and dom.peak == FP4_PEAK_TFLOPS and not args.profile_stage and not args.no_cold:
         # context: the FP4 MFMA rate this GPU sustains with random operands (power-limited clock), and the
         # kernel's executed (dense-masked) rate as a fraction of it
         sustained = mfma_sustained_rate(torch)
@@ -533,7 +579,7 @@ def main():
         "metric": "SharQ linear tokens/s (prepare GB/s and FP4 GEMM TFLOP/s as fractions of MI355X peak)",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "mxfp4", "data": "synthetic", "config": cfg, "roofline": roof, "stages": breakdown,
+        "dtype": cfg.get("format", "mxfp4"), "data": "synthetic", "config": cfg, "roofline": roof, "stages": breakdown,
     }
     if not args.profile_stage and not args.no_cold:
         line["hbm_copy_GBps"] = copy_rate(torch)

@@ -355,6 +355,63 @@ SHARQ_API int sharq_moe_combine(const float* y, int64_t P, int64_t H,
 SHARQ_API int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h,
                    hipStream_t stream);
 
+/*
+ * NVFP4 (SharQ page, Abstract: the method generalises to NVFP4 as well as
+ * MXFP4). The pages name NVFP4 without defining it; its public definition is
+ * used: E2M1 codes in blocks of 16 consecutive K entries, one FP8 E4M3
+ * (OCP E4M3FN) scale byte per block, one fp32 scale per tensor, so an entry
+ * decodes to e2m1(code) * e4m3(scale byte) * tensor_scale. Coding of a block
+ * (fp32, round to nearest even): v = amax / fp32(6 * tensor_scale); scale =
+ * the E4M3 value nearest to v (ties to the even code, 448 above 448);
+ * d = fp32(e4m3(scale) * tensor_scale); code = E2M1 code nearest to
+ * fp32(x / d), saturated at 6, sign kept on zero (all signed zeros if d == 0).
+ * Layout: stage-major as above with codes u8 [G][R][64] (the same byte and
+ * nibble positions) and scales u8 [G][R][8]: the E4M3 byte of 16-block j of
+ * stage g of row r at [g][r][j]. Bytes past K are zero.
+ * tensor_scale must be finite and > 0 (SHARQ_EINVAL otherwise); the usual
+ * choice is amax / (6 * 448) of the tensor (a calibration the caller makes).
+ */
+
+/*
+ * sharq_prepare_nvfp4 -- sharq_prepare with NVFP4 codes. The activation has
+ * one tensor scale shared by backbone and residual (each has its own block
+ * scales). The residual is r = fp32(x' - fp32(e2m1 * e4m3 * tensor_scale)).
+ *  bb_codes, res_codes    u8 [G][T][64]
+ *  bb_scales, res_scales  u8 [G][T][8] (E4M3 bytes)
+ *  other arguments and requirements as sharq_prepare.
+ */
+SHARQ_API int sharq_prepare_nvfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx,
+                        const uint16_t* gamma, int n, int m, float tensor_scale,
+                        uint8_t* bb_codes, uint8_t* bb_scales,
+                        uint8_t* res_codes, uint8_t* res_scales,
+                        uint8_t* mask, hipStream_t stream);
+
+/*
+ * sharq_quantize_nvfp4 -- NVFP4 of a bf16 weight w [O][ldw] (first K entries
+ * of each row) with tensor scale tensor_scale: codes u8 [G][O][64], scales
+ * u8 [G][O][8]. Requirements as sharq_quantize_mxfp4.
+ */
+SHARQ_API int sharq_quantize_nvfp4(const uint16_t* w, int64_t O, int64_t K, int64_t ldw,
+                         float tensor_scale, uint8_t* codes, uint8_t* scales,
+                         hipStream_t stream);
+
+/*
+ * sharq_linear_nvfp4 -- the two-path GEMM on NVFP4 operands:
+ *   Y = deq(A_s) deq(W)^T + deq(A_r) deq(W)^T   (fp32 accumulation),
+ * A_s, A_r with tensor scale a_tensor_scale, W with w_tensor_scale.
+ * The codes are widened to fp16 (code * block scale is exact there) and
+ * multiplied on the fp16 matrix cores.
+ *  bb_*, res_*   as written by sharq_prepare_nvfp4 ([G][T][64], [G][T][8]);
+ *  w_codes u8 [G][O][64], w_scales u8 [G][O][8];  y fp32 [T][ldy].
+ * Requires K % 32 == 0, ldy >= O, ceil(T/128) * ceil(O/256) <= 2^24.
+ */
+SHARQ_API int sharq_linear_nvfp4(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                       const uint8_t* res_codes, const uint8_t* res_scales,
+                       float a_tensor_scale, const uint8_t* w_codes,
+                       const uint8_t* w_scales, float w_tensor_scale,
+                       int64_t T, int64_t O, int64_t K, float* y, int64_t ldy,
+                       hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

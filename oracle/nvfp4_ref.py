@@ -118,7 +118,7 @@ def nvfp4_quantize(vals: np.ndarray, s_t, keep: np.ndarray | None = None):
     sb = e4m3_encode(v)
     d = (e4m3_decode(sb).astype(np.float32) * s_t).astype(np.float32)  # [T, nb]
     d_full = np.repeat(d, NV_BLOCK, axis=1)
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         q = np.where(d_full > 0, vals / np.where(d_full > 0, d_full, np.float32(1)), np.float32(0))
     q = q.astype(np.float32)
     # beyond 6 every value codes as 6; an fp32 overflow of x / d (tiny d) is one

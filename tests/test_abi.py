@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 6
+    assert _lib.call("sharq_abi_version") == 7
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
@@ -275,3 +275,31 @@ def test_moe_combine_validation():
     assert call(A + 4, 8, 16, B, C, 4, 2, D, 0, 0) == _lib.SHARQ_EALIGN
     assert call(A, 8, 16, B, C, 4, 2, 0, D + 4, 0) == _lib.SHARQ_EALIGN   # bf16 output needs 8 bytes
     assert call(A, 8, 16, B + 2, C, 4, 2, D, 0, 0) == _lib.SHARQ_EALIGN
+
+
+def test_nvfp4_validation():
+    prep = lambda T=4, K=64, ldx=64, s=1.0, n=2, m=4, x=A, bs=C: _lib.call(
+        "sharq_prepare_nvfp4", x, T, K, ldx, 0, n, m, s, B, bs, D, E_, F, 0)
+    assert prep(T=0) == _lib.SHARQ_OK
+    assert prep(s=0.0) == _lib.SHARQ_EINVAL             # tensor scale must be > 0
+    assert prep(s=-1.0) == _lib.SHARQ_EINVAL
+    assert prep(s=float("inf")) == _lib.SHARQ_EINVAL
+    assert prep(s=float("nan")) == _lib.SHARQ_EINVAL
+    assert prep(K=48, ldx=48) == _lib.SHARQ_EINVAL      # K % 32
+    assert prep(n=4, m=8) == _lib.SHARQ_EUNSUPPORTED
+    assert prep(x=0) == _lib.SHARQ_EINVAL
+    assert prep(bs=C + 8) == _lib.SHARQ_EALIGN
+    q = lambda O=4, K=64, ldw=64, s=1.0, w=A: _lib.call("sharq_quantize_nvfp4", w, O, K, ldw, s, B, C, 0)
+    assert q(O=0) == _lib.SHARQ_OK
+    assert q(s=0.0) == _lib.SHARQ_EINVAL
+    assert q(K=40, ldw=40) == _lib.SHARQ_EINVAL
+    assert q(w=A + 2) == _lib.SHARQ_EALIGN
+    lin = lambda T=4, O=8, K=64, ldy=8, sa=1.0, sw=1.0, y=G: _lib.call(
+        "sharq_linear_nvfp4", A, B, C, D, sa, E_, F, sw, T, O, K, y, ldy, 0)
+    assert lin(T=0) == _lib.SHARQ_OK
+    assert lin(sa=0.0) == _lib.SHARQ_EINVAL
+    assert lin(sw=float("inf")) == _lib.SHARQ_EINVAL
+    assert lin(ldy=4) == _lib.SHARQ_EINVAL
+    assert lin(K=48) == _lib.SHARQ_EINVAL
+    assert lin(y=G + 4) == _lib.SHARQ_EALIGN
+    assert lin(T=1 << 30, O=1 << 30) == _lib.SHARQ_EINVAL  # grid bound

@@ -3,7 +3,8 @@
 // dense FP4 peak assumes the top clock; with realistic (random) operands the
 // matrix cores draw enough power that the clock drops, so the rate a kernel
 // can reach is lower. The benchmark reports this figure beside the published
-// peak. Not part of the SharQ library: it is built as its own shared object.
+// peak (and the same for the fp16 MFMA). Not part of the SharQ library: it is
+// built as its own shared object.
 //
 // Each wave issues chains of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4) on
 // operands filled from a per-lane hash (random bit patterns, so every
@@ -53,7 +54,42 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(int iterations, uint32_t
   if ((threadIdx.x & 63) == 0) out[gid >> 6] = s;
 }
 
+// The same for V_MFMA_F32_32X32X16_F16 (the unit the NVFP4 GEMM runs on):
+// random fp16 operands with exponents kept near 1 so no product overflows.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+__global__ __launch_bounds__(256) void mfma_rate_f16_kernel(int iterations, uint32_t seed, float* __restrict__ out) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  v8h a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t ra = mix(seed ^ (gid * 16 + i)), rb = mix(seed ^ (gid * 16 + 8 + i) ^ 0x9e3779b9u);
+    // sign and 10 mantissa bits random, exponent field 14 or 15 (values in [0.5, 2))
+    a[i] = __builtin_bit_cast(_Float16, (uint16_t)((ra & 0x83FFu) | ((14u + ((ra >> 16) & 1u)) << 10)));
+    b[i] = __builtin_bit_cast(_Float16, (uint16_t)((rb & 0x83FFu) | ((14u + ((rb >> 16) & 1u)) << 10)));
+  }
+  v16f acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = v16f{};
+  for (int it = 0; it < iterations; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  if ((threadIdx.x & 63) == 0) out[gid >> 6] = s;
+}
+
 }  // namespace
+
+extern "C" __attribute__((visibility("default"))) int sharq_calib_mfma_f16(int blocks, int iterations,
+                                                                             float* out, hipStream_t stream) {
+  if (blocks <= 0 || iterations <= 0 || !out) return -1;
+  hipLaunchKernelGGL(mfma_rate_f16_kernel, dim3(blocks), dim3(256), 0, stream, iterations, 0x1234567u, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 extern "C" __attribute__((visibility("default"))) int sharq_calib_mfma_fp4(int blocks, int iterations,
                                                                              float* out, hipStream_t stream) {

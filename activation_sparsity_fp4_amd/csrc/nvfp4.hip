@@ -64,8 +64,20 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
+// fp32(x / d), the correctly rounded quotient, from rd = fp64(1 / d): the
+// exact quotient of two fp32 numbers is either an fp32 rounding midpoint's
+// neighbour at a relative distance of at least 2^-49 or not near one at all
+// (x - M d is a non-zero multiple of M d's last bit, and it cannot be zero
+// since M's odd 25-bit significand cannot divide x's 24-bit one), while
+// fp64(x * rd) is within a relative 2^-52 + 2^-106 of it; rounding that to
+// fp32 therefore gives the same result. Quotients in the fp32 subnormal range
+// are far below E2M1's first midpoint (0.25), so they code as a signed zero
+// either way. One fp64 multiply per entry instead of a division sequence.
+__device__ __forceinline__ float nv_quotient(float x, double rd) { return (float)((double)x * rd); }
+
 // E2M1 codes of 16 entries (8 bytes, low nibble first) for divisor d.
 __device__ __forceinline__ uint2 nv_codes16(const float* v, float d) {
+  const double rd = 1.0 / (double)d;
   uint32_t w[2];
 #pragma unroll
   for (int dw = 0; dw < 2; ++dw) {
@@ -73,10 +85,10 @@ __device__ __forceinline__ uint2 nv_codes16(const float* v, float d) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       float q0 = v[8 * dw + 2 * p], q1 = v[8 * dw + 2 * p + 1];
-      // x / d correctly rounded; d == 0 leaves a signed zero. Values past 6
-      // (an fp32 overflow included) saturate to 6 in the converter.
-      q0 = d > 0.0f ? fminf(fmaxf(q0 / d, -7.0f), 7.0f) : q0 * 0.0f;
-      q1 = d > 0.0f ? fminf(fmaxf(q1 / d, -7.0f), 7.0f) : q1 * 0.0f;
+      // x / d as fp32; d == 0 leaves a signed zero. Values past 6 (an fp32
+      // overflow included) saturate to 6 in the converter.
+      q0 = d > 0.0f ? fminf(fmaxf(nv_quotient(q0, rd), -7.0f), 7.0f) : q0 * 0.0f;
+      q1 = d > 0.0f ? fminf(fmaxf(nv_quotient(q1, rd), -7.0f), 7.0f) : q1 * 0.0f;
       switch (p) {
         case 0: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q0, q1, 1.0f, 0); break;
         case 1: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q0, q1, 1.0f, 1); break;
@@ -276,48 +288,53 @@ __device__ __forceinline__ void nv_store_stage(uint8_t* lds, int tid, const NvSt
   *reinterpret_cast<uint2*>(lds + kNvOffSW + tid * 8) = r.s[1];
 }
 
-// The lane's 32 code bytes of one row (K entries 64 h .. 64 h + 63 of the
-// stage, h = lane / 32) and its 4 block scales as fp16 values times 2^-4.
-struct NvRow {
-  uint32_t c[8];
+// A lane's block scales of one row for the stage: the 4 blocks covering K
+// entries 64 h .. 64 h + 63 (h = lane / 32), as fp16 values times 2^-4.
+struct NvScales {
   v2h s01, s23;
 };
 
-__device__ __forceinline__ NvRow nv_read_row(const uint8_t* lds, int code_off, int scale_off, int row, int h) {
-  NvRow r;
-  const uint4 lo = *reinterpret_cast<const uint4*>(lds + code_off + row * 64 + nv_chunk(row, 2 * h) * 16);
-  const uint4 hi = *reinterpret_cast<const uint4*>(lds + code_off + row * 64 + nv_chunk(row, 2 * h + 1) * 16);
-  r.c[0] = lo.x; r.c[1] = lo.y; r.c[2] = lo.z; r.c[3] = lo.w;
-  r.c[4] = hi.x; r.c[5] = hi.y; r.c[6] = hi.z; r.c[7] = hi.w;
+__device__ __forceinline__ NvScales nv_read_scales(const uint8_t* lds, int scale_off, int row, int h) {
   const uint32_t s = *reinterpret_cast<const uint32_t*>(lds + scale_off + row * 8 + 4 * h);
-  r.s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 0.0625f, false);
-  r.s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 0.0625f, true);
-  return r;
+  return NvScales{__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 0.0625f, false),
+                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 0.0625f, true)};
 }
 
-// MFMA operand of k-step ks: the lane's 8 entries 64 h + 8 ks .. + 7 (inside
-// block ks / 2 of its four), each E2M1 value times the block scale.
+// The lane's 16 code bytes of k-step quad Q (k-steps 4 Q .. 4 Q + 3: K entries
+// 64 h + 32 Q .. + 31) of one row.
+template <int Q>
+__device__ __forceinline__ uint4 nv_read_codes(const uint8_t* lds, int code_off, int row, int h) {
+  return *reinterpret_cast<const uint4*>(lds + code_off + row * 64 + nv_chunk(row, 2 * h + Q) * 16);
+}
+
+// MFMA operand of k-step KS: the lane's 8 entries 64 h + 8 KS .. + 7 (inside
+// its block KS / 2), each E2M1 value times the block scale.
 template <int KS>
-__device__ __forceinline__ v8h nv_frag(const NvRow& r) {
-  const _Float16 sh = (KS >> 1) == 0 ? r.s01[0] : (KS >> 1) == 1 ? r.s01[1] : (KS >> 1) == 2 ? r.s23[0] : r.s23[1];
+__device__ __forceinline__ v8h nv_frag(uint32_t word, const NvScales& s) {
+  const _Float16 sh = (KS >> 1) == 0 ? s.s01[0] : (KS >> 1) == 1 ? s.s01[1] : (KS >> 1) == 2 ? s.s23[0] : s.s23[1];
   const v2h s2 = {sh, sh};
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[KS], 1.0f, 0) * s2;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[KS], 1.0f, 1) * s2;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[KS], 1.0f, 2) * s2;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(r.c[KS], 1.0f, 3) * s2;
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * s2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * s2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * s2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * s2;
   return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
+__device__ __forceinline__ uint32_t nv_word(const uint4& c, int i) {
+  return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w;
+}
+
 template <int KS>
-__device__ __forceinline__ void nv_kstep(const NvRow (&as)[2], const NvRow (&ar)[2], const NvRow (&w)[4],
+__device__ __forceinline__ void nv_kstep(const uint4 (&cs)[2], const uint4 (&cr)[2], const uint4 (&cw)[4],
+                                         const NvScales (&ss)[2], const NvScales (&sr)[2], const NvScales (&sw)[4],
                                          v16f (&acc)[2][4]) {
   v8h fw[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) fw[j] = nv_frag<KS>(w[j]);
+  for (int j = 0; j < 4; ++j) fw[j] = nv_frag<KS>(nv_word(cw[j], KS & 3), sw[j]);
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const v8h fs = nv_frag<KS>(as[i]);
-    const v8h fr = nv_frag<KS>(ar[i]);
+    const v8h fs = nv_frag<KS>(nv_word(cs[i], KS & 3), ss[i]);
+    const v8h fr = nv_frag<KS>(nv_word(cr[i], KS & 3), sr[i]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fs, fw[j], acc[i][j], 0, 0, 0);
@@ -326,24 +343,41 @@ __device__ __forceinline__ void nv_kstep(const NvRow (&as)[2], const NvRow (&ar)
   }
 }
 
-__device__ __forceinline__ void nv_compute_stage(const uint8_t* lds, int wm, int wn, int r32, int h,
-                                                 v16f (&acc)[2][4]) {
-  NvRow as[2], ar[2], w[4];
+template <int Q>
+__device__ __forceinline__ void nv_quad(const uint8_t* lds, const int (&ra)[2], const int (&rw)[4], int h,
+                                        const NvScales (&ss)[2], const NvScales (&sr)[2], const NvScales (&sw)[4],
+                                        v16f (&acc)[2][4]) {
+  uint4 cs[2], cr[2], cw[4];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    as[i] = nv_read_row(lds, kNvOffAs, kNvOffSAs, wm * 64 + i * 32 + r32, h);
-    ar[i] = nv_read_row(lds, kNvOffAr, kNvOffSAr, wm * 64 + i * 32 + r32, h);
+    cs[i] = nv_read_codes<Q>(lds, kNvOffAs, ra[i], h);
+    cr[i] = nv_read_codes<Q>(lds, kNvOffAr, ra[i], h);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = nv_read_row(lds, kNvOffW, kNvOffSW, wn * 128 + j * 32 + r32, h);
-  nv_kstep<0>(as, ar, w, acc);
-  nv_kstep<1>(as, ar, w, acc);
-  nv_kstep<2>(as, ar, w, acc);
-  nv_kstep<3>(as, ar, w, acc);
-  nv_kstep<4>(as, ar, w, acc);
-  nv_kstep<5>(as, ar, w, acc);
-  nv_kstep<6>(as, ar, w, acc);
-  nv_kstep<7>(as, ar, w, acc);
+  for (int j = 0; j < 4; ++j) cw[j] = nv_read_codes<Q>(lds, kNvOffW, rw[j], h);
+  nv_kstep<4 * Q + 0>(cs, cr, cw, ss, sr, sw, acc);
+  nv_kstep<4 * Q + 1>(cs, cr, cw, ss, sr, sw, acc);
+  nv_kstep<4 * Q + 2>(cs, cr, cw, ss, sr, sw, acc);
+  nv_kstep<4 * Q + 3>(cs, cr, cw, ss, sr, sw, acc);
+}
+
+__device__ __forceinline__ void nv_compute_stage(const uint8_t* lds, int wm, int wn, int r32, int h,
+                                                 v16f (&acc)[2][4]) {
+  int ra[2], rw[4];
+  NvScales ss[2], sr[2], sw[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    ra[i] = wm * 64 + i * 32 + r32;
+    ss[i] = nv_read_scales(lds, kNvOffSAs, ra[i], h);
+    sr[i] = nv_read_scales(lds, kNvOffSAr, ra[i], h);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    rw[j] = wn * 128 + j * 32 + r32;
+    sw[j] = nv_read_scales(lds, kNvOffSW, rw[j], h);
+  }
+  nv_quad<0>(lds, ra, rw, h, ss, sr, sw, acc);
+  nv_quad<1>(lds, ra, rw, h, ss, sr, sw, acc);
 }
 
 // Tile order: each XCD (workgroups are dealt round-robin over 8) gets a

@@ -408,21 +408,22 @@ def copy_rate(torch, n_bytes=1 << 30, reps=10):
     return round(2 * n_bytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
 
 
-def mfma_sustained_rate(torch, reps=5):
-    """TFLOP/s of the scaled FP4 MFMA this GPU sustains on register operands
-    with random bit patterns (no memory traffic; libsharq_calib.so, built
-    beside the library): the rate a GEMM can reach once the power-limited
-    clock is taken into account, reported beside the published peak."""
+def mfma_sustained_rate(torch, reps=5, unit="fp4"):
+    """TFLOP/s of the scaled FP4 MFMA (unit "fp4") or the fp16 MFMA (unit
+    "f16") this GPU sustains on register operands with random bit patterns (no
+    memory traffic; libsharq_calib.so, built beside the library): the rate a
+    GEMM can reach once the power-limited clock is taken into account,
+    reported beside the published peak."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "activation_sparsity_fp4_amd", "libsharq_calib.so"))
-    fn = lib.sharq_calib_mfma_fp4
+    fn = lib.sharq_calib_mfma_fp4 if unit == "fp4" else lib.sharq_calib_mfma_f16
     fn.restype = ctypes.c_int
     fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     props = torch.cuda.get_device_properties(0)
     blocks, iters = 2 * props.multi_processor_count, 4000
     out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    flops = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * 64
+    flops = blocks * 4 * iters * 8 * 2.0 * 32 * 32 * (64 if unit == "fp4" else 16)
     ts = []
     for k in range(reps + 2):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -564,10 +565,10 @@ def main():
         roof = {"kernel": dom.name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "us_per_launch": round(dom_ms * 1e3, 2)}
-    if dom.kind == "mfma" and dom.peak == FP4_PEAK_TFLOPS and not args.profile_stage and not args.no_cold:
-        # context: the FP4 MFMA rate this GPU sustains with random operands (power-limited clock), and the
+    if dom.kind == "mfma" and not args.profile_stage and not args.no_cold:
+        # context: the MFMA rate this GPU sustains with random operands (power-limited clock), and the
         # kernel's executed (dense-masked) rate as a fraction of it
-        sustained = mfma_sustained_rate(torch)
+        sustained = mfma_sustained_rate(torch, unit="fp4" if dom.peak == FP4_PEAK_TFLOPS else "f16")
         roof["sustained_mfma_TFLOPs"] = sustained
         roof["frac_exec_of_sustained"] = round(dom.flops_exec / (dom_ms * 1e-3) / 1e12 / sustained, 4)
     if traffic is not None:

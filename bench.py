@@ -476,6 +476,8 @@ def main():
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache stage timing")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device copy of this many bytes (reference for counter scaling)")
+    ap.add_argument("--calib", choices=["fp4", "f16"], default=None,
+                    help="only run the MFMA rate calibration kernel (reference for clock and MFMA-busy counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -487,6 +489,10 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs the GPU")
     torch.cuda.init()
+    if args.calib:
+        import torch
+        print(json.dumps({"calib": args.calib, "TFLOP/s": mfma_sustained_rate(torch, unit=args.calib)}), flush=True)
+        return
     if args.copy_bytes:
         copy_calibration(args.copy_bytes, args.steps)
         return

@@ -77,18 +77,19 @@ __device__ __forceinline__ float nv_quotient(float x, double rd) { return (float
 
 // E2M1 codes of 16 entries (8 bytes, low nibble first) for divisor d.
 __device__ __forceinline__ uint2 nv_codes16(const float* v, float d) {
-  const double rd = 1.0 / (double)d;
+  // d == 0: a reciprocal of 0 makes every quotient x * 0, a signed zero
+  const double rd = d > 0.0f ? 1.0 / (double)d : 0.0;
   uint32_t w[2];
 #pragma unroll
   for (int dw = 0; dw < 2; ++dw) {
     uint32_t r = 0;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      float q0 = v[8 * dw + 2 * p], q1 = v[8 * dw + 2 * p + 1];
-      // x / d as fp32; d == 0 leaves a signed zero. Values past 6 (an fp32
-      // overflow included) saturate to 6 in the converter.
-      q0 = d > 0.0f ? fminf(fmaxf(nv_quotient(q0, rd), -7.0f), 7.0f) : q0 * 0.0f;
-      q1 = d > 0.0f ? fminf(fmaxf(nv_quotient(q1, rd), -7.0f), 7.0f) : q1 * 0.0f;
+      // x / d as fp32, clamped to [-7, 7] (one median; signed zeros pass);
+      // the converter saturates everything past 6 to 6, an fp32 overflow
+      // of the quotient included
+      const float q0 = __builtin_amdgcn_fmed3f(nv_quotient(v[8 * dw + 2 * p], rd), -7.0f, 7.0f);
+      const float q1 = __builtin_amdgcn_fmed3f(nv_quotient(v[8 * dw + 2 * p + 1], rd), -7.0f, 7.0f);
       switch (p) {
         case 0: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q0, q1, 1.0f, 0); break;
         case 1: r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, q0, q1, 1.0f, 1); break;

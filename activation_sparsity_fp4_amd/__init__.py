@@ -105,6 +105,17 @@ def _check_stage_major(codes, scales, R, K, name):
         raise ValueError(f"{name}: codes and scales must be contiguous")
 
 
+def _check_matrix(t, dtype, rows, cols, name, contiguous=False):
+    """A [rows, cols] device tensor of dtype with unit column stride (and
+    contiguous rows when the entry point takes no leading dimension): the
+    kernels write rows x cols entries through it, so nothing smaller passes."""
+    _need(t, dtype, name, 2)
+    if tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name}: expected shape ({rows}, {cols}), got {tuple(t.shape)}")
+    if t.stride(1) != 1 or (contiguous and not t.is_contiguous()):
+        raise ValueError(f"{name} must be {'contiguous' if contiguous else 'contiguous along its rows'}")
+
+
 def _check_prepared(prep):
     torch = _torch()
     for name in ("bb_codes", "res_codes", "bb_scales", "res_scales"):
@@ -112,6 +123,8 @@ def _check_prepared(prep):
     T = prep.bb_codes.shape[1]
     _check_stage_major(prep.bb_codes, prep.bb_scales, T, prep.K, "backbone")
     _check_stage_major(prep.res_codes, prep.res_scales, T, prep.K, "residual")
+    if prep.mask is not None:
+        _check_matrix(prep.mask, torch.uint8, T, prep.K // 8, "mask", contiguous=True)
 
 
 def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: Optional[Prepared] = None,
@@ -134,11 +147,18 @@ def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: 
                        torch.empty((G, T, 64), **kw), torch.empty((G, T, 4), **kw),
                        torch.empty((T, K // 8), **kw) if with_mask else None, K,
                        torch.empty((T,), dtype=torch.float32, device=x.device) if rms_eps is not None else None)
-    elif out.K != K:
-        raise ValueError("out was allocated for another K")
+    else:
+        if out.K != K:
+            raise ValueError("out was allocated for another K")
+        _check_prepared(out)
+        if out.bb_codes.shape[1] != T:
+            raise ValueError("out was allocated for another number of rows")
     if rms_eps is not None:
         if out.rms_scale is None:
             raise ValueError("out has no rms_scale buffer")
+        _need(out.rms_scale, torch.float32, "rms_scale", 1)
+        if out.rms_scale.numel() != T or not out.rms_scale.is_contiguous():
+            raise ValueError("rms_scale must be a contiguous fp32 [T] tensor")
         st = _lib.call("sharq_prepare_rms", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), float(rms_eps), n, m,
                        out.rms_scale.data_ptr(), out.bb_codes.data_ptr(), out.bb_scales.data_ptr(),
                        out.res_codes.data_ptr(), out.res_scales.data_ptr(), _ptr(out.mask), _stream(x.device))
@@ -171,6 +191,9 @@ def quantize_mxfp4(x, out: Optional[MXFP4] = None) -> MXFP4:
     if out is None:
         out = MXFP4(torch.empty((stages(K), R, 64), dtype=torch.uint8, device=x.device),
                     torch.empty((stages(K), R, 4), dtype=torch.uint8, device=x.device), K)
+    _need(out.codes, torch.uint8, "out.codes", 3)
+    _need(out.scales, torch.uint8, "out.scales", 3)
+    _check_stage_major(out.codes, out.scales, R, K, "out")
     st = _lib.call("sharq_quantize_mxfp4", x.data_ptr(), R, K, x.stride(0), out.codes.data_ptr(),
                    out.scales.data_ptr(), _stream(x.device))
     _lib.check("sharq_quantize_mxfp4", st)
@@ -207,7 +230,7 @@ def linear(prep: Prepared, w: MXFP4, out=None, split_k: bool = True):
     _check_stage_major(w.codes, w.scales, O, K, "w")
     if out is None:
         out = torch.empty((T, O), dtype=torch.float32, device=prep.bb_codes.device)
-    _need(out, torch.float32, "out", 2)
+    _check_matrix(out, torch.float32, T, O, "out")
     nbytes = _lib.call("sharq_linear_workspace_bytes", T, O, K) if split_k else 0
     if nbytes > 0:
         ws = _workspace(out.device, nbytes)
@@ -245,6 +268,7 @@ def linear_grouped(prep: Prepared, w: MXFP4, seg_offsets, a_rows=None, out=None)
         P = prep.bb_codes.shape[1]
     if out is None:
         out = torch.empty((P, O), dtype=torch.float32, device=w.codes.device)
+    _check_matrix(out, torch.float32, P, O, "out", contiguous=True)
     st = _lib.call("sharq_linear_grouped", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
                    prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), prep.bb_codes.shape[1], _ptr(a_rows),
                    seg_offsets.data_ptr(), E, w.codes.data_ptr(), w.scales.data_ptr(), P, O, K, out.data_ptr(),
@@ -407,6 +431,11 @@ def expand_backbone(cb: CompactBackbone, bb_codes=None, mask=None, with_mask: bo
         mask = torch.empty((T, K // 8), dtype=torch.uint8, device=dev)
     if not with_mask:
         mask = None
+    _need(bb_codes, torch.uint8, "bb_codes", 3)
+    if tuple(bb_codes.shape) != (stages(K), T, 64) or not bb_codes.is_contiguous():
+        raise ValueError(f"bb_codes must be a contiguous [{stages(K)}, {T}, 64] tensor")
+    if mask is not None:
+        _check_matrix(mask, torch.uint8, T, K // 8, "mask", contiguous=True)
     st = _lib.call("sharq_expand_backbone", cb.codes.data_ptr(), cb.meta.data_ptr(), T, K, cb.n, cb.m,
                    bb_codes.data_ptr(), _ptr(mask), _stream(dev))
     _lib.check("sharq_expand_backbone", st)
@@ -429,7 +458,7 @@ def moe_combine(y, pair_index, weights, out=None, bf16: bool = False):
     dt = torch.bfloat16 if bf16 else torch.float32
     if out is None:
         out = torch.empty((T, H), dtype=dt, device=y.device)
-    _need(out, dt, "out", 2)
+    _check_matrix(out, dt, T, H, "out", contiguous=True)
     st = _lib.call("sharq_moe_combine", y.data_ptr(), P, H, pair_index.data_ptr(), weights.data_ptr(), T, k,
                    0 if bf16 else out.data_ptr(), out.data_ptr() if bf16 else 0, _stream(y.device))
     _lib.check("sharq_moe_combine", st)
@@ -446,6 +475,7 @@ def silu_mul(gu, out=None):
     I = I2 // 2
     if out is None:
         out = torch.empty((T, I), dtype=torch.bfloat16, device=gu.device)
+    _check_matrix(out, torch.bfloat16, T, I, "out", contiguous=True)
     st = _lib.call("sharq_silu_mul", gu.data_ptr(), T, I, out.data_ptr(), _stream(gu.device))
     _lib.check("sharq_silu_mul", st)
     return out
@@ -507,9 +537,13 @@ def prepare_nvfp4(x, tensor_scale: float, gamma=None, n: int = 2, m: int = 4, wi
         out = NVPrepared(torch.empty((G, T, 64), **kw), torch.empty((G, T, 8), **kw),
                          torch.empty((G, T, 64), **kw), torch.empty((G, T, 8), **kw),
                          torch.empty((T, K // 8), **kw) if with_mask else None, K, float(tensor_scale))
-    elif out.K != K:
-        raise ValueError("out was allocated for another K")
     else:
+        if out.K != K:
+            raise ValueError("out was allocated for another K")
+        _check_nv(out.bb_codes, out.bb_scales, T, K, "out backbone")
+        _check_nv(out.res_codes, out.res_scales, T, K, "out residual")
+        if out.mask is not None:
+            _check_matrix(out.mask, torch.uint8, T, K // 8, "out.mask", contiguous=True)
         out = out._replace(tensor_scale=float(tensor_scale))
     st = _lib.call("sharq_prepare_nvfp4", x.data_ptr(), T, K, x.stride(0), _ptr(gamma), n, m, float(tensor_scale),
                    out.bb_codes.data_ptr(), out.bb_scales.data_ptr(), out.res_codes.data_ptr(),
@@ -529,6 +563,7 @@ def quantize_nvfp4(w, tensor_scale: float, out: Optional[NVFP4] = None) -> NVFP4
         out = NVFP4(torch.empty((stages(K), O, 64), dtype=torch.uint8, device=w.device),
                     torch.empty((stages(K), O, 8), dtype=torch.uint8, device=w.device), K, float(tensor_scale))
     else:
+        _check_nv(out.codes, out.scales, O, K, "out")
         out = out._replace(tensor_scale=float(tensor_scale))
     st = _lib.call("sharq_quantize_nvfp4", w.data_ptr(), O, K, w.stride(0), float(tensor_scale),
                    out.codes.data_ptr(), out.scales.data_ptr(), _stream(w.device))
@@ -548,7 +583,7 @@ def linear_nvfp4(prep: NVPrepared, w: NVFP4, out=None):
         raise ValueError("weight K does not match the activation K")
     if out is None:
         out = torch.empty((T, O), dtype=torch.float32, device=prep.bb_codes.device)
-    _need(out, torch.float32, "out", 2)
+    _check_matrix(out, torch.float32, T, O, "out")
     st = _lib.call("sharq_linear_nvfp4", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
                    prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), float(prep.tensor_scale),
                    w.codes.data_ptr(), w.scales.data_ptr(), float(w.tensor_scale), T, O, K, out.data_ptr(),

@@ -239,11 +239,17 @@ __device__ __forceinline__ void read_item(const uint8_t* st, Frags<C>& f, Scales
 
 // MFMA number M of a sub-step, path-major (both paths of an accumulator are
 // 2 WM WN / 2 MFMAs apart, so no MFMA waits on the one before it).
-template <class C, int SUB, int M>
-__device__ __forceinline__ void mfma_one(const Frags<C>& f, const Scales<C>& c, v16f (&acc)[C::WM][C::WN]) {
+// kSkip: the wave's row blocks from `active` on hold no valid row of the tile
+// (a partial last row tile of an expert segment); their MFMAs are skipped, a
+// wave-uniform branch (their accumulators stay zero, and no row of theirs is
+// stored).
+template <class C, int SUB, int M, bool kSkip>
+__device__ __forceinline__ void mfma_one(const Frags<C>& f, const Scales<C>& c, v16f (&acc)[C::WM][C::WN],
+                                         int active) {
   constexpr int p = M / (C::WM * C::WN), i = (M % (C::WM * C::WN)) / C::WN, j = M % C::WN;
-  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[p][i], f.w[j], acc[i][j], 4, 4, 2 * SUB,
-                                                              (int)c.a[p][i], 2 * SUB, (int)c.w[j]);
+  if (!kSkip || i < active)
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[p][i], f.w[j], acc[i][j], 4, 4, 2 * SUB,
+                                                                (int)c.a[p][i], 2 * SUB, (int)c.w[j]);
 }
 
 // ---------------------------------------------------------------------------
@@ -370,51 +376,51 @@ __device__ __forceinline__ void ring_barrier() {
 // Every iteration has the same shape (batches past the last stage are issued
 // with out-of-range offsets and read nothing), so the vmcnt bound is a
 // constant and no branch splits the MFMA groups from the barrier.
-template <class C, int M>
+template <class C, int M, bool kSkip>
 __device__ __forceinline__ void ring_first_half(const Frags<C>& f0, const Scales<C>& c, v16f (&acc)[C::WM][C::WN],
                                                 const uint8_t* cur, Frags<C>& f1, Scales<C>& unused, int wm, int wn,
-                                                int lr, int lh) {
+                                                int lr, int lh, int active) {
   if constexpr (M < 2 * C::WM * C::WN) {
-    mfma_one<C, 0, M>(f0, c, acc);
+    mfma_one<C, 0, M, kSkip>(f0, c, acc, active);
     read_item<C, 1, M>(cur, f1, unused, wm, wn, lr, lh);
     __builtin_amdgcn_sched_barrier(0);
-    ring_first_half<C, M + 1>(f0, c, acc, cur, f1, unused, wm, wn, lr, lh);
+    ring_first_half<C, M + 1, kSkip>(f0, c, acc, cur, f1, unused, wm, wn, lr, lh, active);
   }
 }
 
-template <class C, int M>
+template <class C, int M, bool kSkip>
 __device__ __forceinline__ void ring_second_half(const Frags<C>& f1, const Scales<C>& c, v16f (&acc)[C::WM][C::WN],
                                                  const RingLoader<C>& ld, const typename RingLoader<C>::Dest& d,
                                                  const uint8_t* next, Frags<C>& f0, Scales<C>& cn, int wm, int wn,
-                                                 int lr, int lh) {
+                                                 int lr, int lh, int active) {
   constexpr int kMfma = 2 * C::WM * C::WN;
   constexpr int kItems = 2 * (2 * C::WM + C::WN);
   if constexpr (M < kMfma || M < C::kLoads || M < kItems) {
-    if constexpr (M < kMfma) mfma_one<C, 1, M>(f1, c, acc);
+    if constexpr (M < kMfma) mfma_one<C, 1, M, kSkip>(f1, c, acc, active);
     ld.template issue_j<M>(d);
     read_item<C, 0, M>(next, f0, cn, wm, wn, lr, lh);
     __builtin_amdgcn_sched_barrier(0);
-    ring_second_half<C, M + 1>(f1, c, acc, ld, d, next, f0, cn, wm, wn, lr, lh);
+    ring_second_half<C, M + 1, kSkip>(f1, c, acc, ld, d, next, f0, cn, wm, wn, lr, lh, active);
   }
 }
 
-template <class C>
+template <class C, bool kSkip>
 __device__ __forceinline__ void ring_iter(const RingLoader<C>& ld, uint8_t* cur, const uint8_t* next, int s,
                                           Frags<C>& f0, Frags<C>& f1, Scales<C>& c, Scales<C>& cn,
-                                          v16f (&acc)[C::WM][C::WN], int wm, int wn, int lr, int lh) {
+                                          v16f (&acc)[C::WM][C::WN], int wm, int wn, int lr, int lh, int active) {
   static_assert(2 * C::WM + C::WN <= 2 * C::WM * C::WN, "every fragment read of sub-step 1 follows an MFMA");
   // a wave issuing its MFMA group gets issue priority over a wave of the
   // other workgroup on the SIMD that is loading or waiting
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(1);
-  ring_first_half<C, 0>(f0, c, acc, cur, f1, cn, wm, wn, lr, lh);
+  ring_first_half<C, 0, kSkip>(f0, c, acc, cur, f1, cn, wm, wn, lr, lh, active);
   __builtin_amdgcn_s_setprio(0);
   wait_vmcnt<(C::kRing - 2) * C::kLoads>();  // batch s+1 landed; later batches may be in flight
   ring_barrier();
   __builtin_amdgcn_sched_barrier(0);
   const typename RingLoader<C>::Dest d = ld.dest(cur, s + C::kRing);
   __builtin_amdgcn_s_setprio(1);
-  ring_second_half<C, 0>(f1, c, acc, ld, d, next, f0, cn, wm, wn, lr, lh);
+  ring_second_half<C, 0, kSkip>(f1, c, acc, ld, d, next, f0, cn, wm, wn, lr, lh, active);
   __builtin_amdgcn_s_setprio(0);
   c = cn;
 }
@@ -423,7 +429,7 @@ __device__ __forceinline__ void ring_iter(const RingLoader<C>& ld, uint8_t* cur,
 // The loop is kept rolled (the slot is a uniform runtime index): unrolling it
 // by the ring length makes the register allocator rotate fragment registers
 // between copies and, at 256 accumulators, spill.
-template <class C>
+template <class C, bool kSkip = false>
 __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows& tr, const TileCols& tc, uint8_t* ring,
                                               v16f (&acc)[C::WM][C::WN], int s_begin, int s_end) {
   const int tid = threadIdx.x;
@@ -432,6 +438,12 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
   const int wm = wave % C::NWM, wn = wave / C::NWM;
   const int lr = lane & 31, lh = lane >> 5;
   const int64_t G = op.nsteps;
+  // row blocks of this wave with at least one valid row (all of them unless kSkip)
+  const int64_t first_row = 32 * C::WM * wm;
+  const int active = __builtin_amdgcn_readfirstlane(
+      !kSkip ? C::WM
+      : tr.rows_valid <= first_row ? 0
+      : (int)min<int64_t>((tr.rows_valid - first_row + 31) / 32, C::WM));
 
   RingLoader<C> ld;
   ld.wave = wave;
@@ -495,7 +507,8 @@ __device__ __forceinline__ void mainloop_ring(const Operands& op, const TileRows
 #pragma unroll 1
   for (int s = s_begin; s < s_end; ++s) {
     const int nslot = slot + 1 == C::kRing ? 0 : slot + 1;
-    ring_iter<C>(ld, ring + slot * C::kStage, ring + nslot * C::kStage, s, f0, f1, c, cn, acc, wm, wn, lr, lh);
+    ring_iter<C, kSkip>(ld, ring + slot * C::kStage, ring + nslot * C::kStage, s, f0, f1, c, cn, acc, wm, wn, lr, lh,
+                        active);
     slot = nslot;
   }
   wait_vmcnt<0>();  // drain the trailing out-of-range batches before the LDS is reused
@@ -864,7 +877,7 @@ __global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) vo
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   if constexpr (kRingPath)
-    mainloop_ring<C>(op, g.tr, TileCols{n0, 0}, lds, acc, 0, op.nsteps);
+    mainloop_ring<C, true>(op, g.tr, TileCols{n0, 0}, lds, acc, 0, op.nsteps);
   else
     mainloop_regs(op, g.tr, n0, lds, lds + C::kStage, acc);
   store_tile<C>(acc, y, op.O, g.tr.m0, g.tr.rows_valid, n0, op.O);
@@ -1052,7 +1065,7 @@ __global__ __launch_bounds__(kThreads, SmallTile::kOccupancy) void linear_groupe
   select_expert(op, g.e, w_codes_all, w_scales_all);
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
-  mainloop_ring<C>(op, g.tr, TileCols{h0, out.I}, lds, acc, 0, op.nsteps);
+  mainloop_ring<C, true>(op, g.tr, TileCols{h0, out.I}, lds, acc, 0, op.nsteps);
   silu_prepare_epilogue<N, M>(acc, lds, g.tr, h0, out);
 }
 

@@ -36,6 +36,9 @@ __all__ = [
     "prepare_nvfp4",
     "quantize_nvfp4",
     "linear_nvfp4",
+    "pack_mxfp4",
+    "pack_nvfp4",
+    "unpack_stage_major",
     "SharqError",
     "status_string",
 ]
@@ -590,3 +593,59 @@ def linear_nvfp4(prep: NVPrepared, w: NVFP4, out=None):
                    out.stride(0), _stream(out.device))
     _lib.check("sharq_linear_nvfp4", st)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Layout conversion: canonical row-major block-FP4 <-> stage-major
+# ---------------------------------------------------------------------------
+
+
+def _pack(codes_rm, scales_rm, K, block, name):
+    torch = _torch()
+    _need(codes_rm, torch.uint8, name + " codes", 2)
+    _need(scales_rm, torch.uint8, name + " scales", 2)
+    R = codes_rm.shape[0]
+    _check_matrix(codes_rm, torch.uint8, R, K // 2, name + " codes", contiguous=True)
+    _check_matrix(scales_rm, torch.uint8, R, K // block, name + " scales", contiguous=True)
+    G = stages(K)
+    codes = torch.empty((G, R, 64), dtype=torch.uint8, device=codes_rm.device)
+    scales = torch.empty((G, R, 128 // block), dtype=torch.uint8, device=codes_rm.device)
+    st = _lib.call("sharq_pack_stage_major", codes_rm.data_ptr(), scales_rm.data_ptr(), R, K, block,
+                   codes.data_ptr(), scales.data_ptr(), _stream(codes_rm.device))
+    _lib.check("sharq_pack_stage_major", st)
+    return codes, scales
+
+
+def pack_mxfp4(codes_rm, scales_rm, K: int) -> MXFP4:
+    """An MXFP4 tensor from the canonical row-major layout (codes [R, K/2],
+    E8M0 scale bytes [R, K/32]), e.g. a weight quantised elsewhere."""
+    codes, scales = _pack(codes_rm, scales_rm, K, 32, "MXFP4")
+    return MXFP4(codes, scales, K)
+
+
+def pack_nvfp4(codes_rm, scales_rm, K: int, tensor_scale: float) -> NVFP4:
+    """An NVFP4 tensor from the canonical row-major layout (codes [R, K/2],
+    E4M3 scale bytes [R, K/16]) and its fp32 tensor scale."""
+    codes, scales = _pack(codes_rm, scales_rm, K, 16, "NVFP4")
+    return NVFP4(codes, scales, K, float(tensor_scale))
+
+
+def unpack_stage_major(codes, scales, K: int):
+    """(codes [R, K/2], scales [R, K/block]) in the canonical row-major layout
+    from stage-major codes [G, R, 64] and scales [G, R, 128/block] (block 32
+    for MXFP4 scales [G, R, 4], 16 for NVFP4 scales [G, R, 8])."""
+    torch = _torch()
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    G, R, _ = codes.shape
+    per = scales.shape[2]
+    if per not in (4, 8) or tuple(codes.shape) != (stages(K), R, 64) or tuple(scales.shape) != (stages(K), R, per) \
+            or not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("expected contiguous stage-major codes [G, R, 64] and scales [G, R, 4 or 8]")
+    block = 128 // per
+    codes_rm = torch.empty((R, K // 2), dtype=torch.uint8, device=codes.device)
+    scales_rm = torch.empty((R, K // block), dtype=torch.uint8, device=codes.device)
+    st = _lib.call("sharq_unpack_stage_major", codes.data_ptr(), scales.data_ptr(), R, K, block,
+                   codes_rm.data_ptr(), scales_rm.data_ptr(), _stream(codes.device))
+    _lib.check("sharq_unpack_stage_major", st)
+    return codes_rm, scales_rm

@@ -31,6 +31,8 @@ SIGNATURES = {
     "sharq_prepare_rms": (_INT, [_P, _I64, _I64, _I64, _P, ctypes.c_float, _INT, _INT, _P, _P, _P, _P, _P, _P,
                                  _P]),
     "sharq_quantize_mxfp4": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "sharq_pack_stage_major": (_INT, [_P, _P, _I64, _I64, _INT, _P, _P, _P]),
+    "sharq_unpack_stage_major": (_INT, [_P, _P, _I64, _I64, _INT, _P, _P, _P]),
     "sharq_prepare_nvfp4": (_INT, [_P, _I64, _I64, _I64, _P, _INT, _INT, ctypes.c_float, _P, _P, _P, _P, _P, _P]),
     "sharq_quantize_nvfp4": (_INT, [_P, _I64, _I64, _I64, ctypes.c_float, _P, _P, _P]),
     "sharq_linear_nvfp4": (_INT, [_P, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _I64, _I64, _I64, _P,

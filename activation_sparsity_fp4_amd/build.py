@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsharq.so")
-SOURCES = ["prepare.hip", "gemm.hip", "glue.hip", "compact.hip", "nvfp4.hip", "sharq_api.hip"]
+SOURCES = ["prepare.hip", "gemm.hip", "glue.hip", "compact.hip", "nvfp4.hip", "layout.hip", "sharq_api.hip"]
 CALIB_SOURCE = "calib.hip"
 CALIB_LIB = os.path.join(PKG, "libsharq_calib.so")
 ARCH = "gfx950"

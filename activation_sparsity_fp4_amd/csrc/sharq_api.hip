@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 // Workgroups of one grouped launch: a one-dimensional grid of 256-thread
 // workgroups whose thread count must stay below 2^32.
 constexpr int64_t kMaxGroupedTiles = (int64_t)1 << 24;
@@ -331,6 +331,39 @@ int sharq_moe_combine(const float* y, int64_t P, int64_t H, const int32_t* pair_
       ((uintptr_t)pair_index & 3u) || ((uintptr_t)weights & 3u))
     return SHARQ_EALIGN;
   return hip_status(sharq::launch_moe_combine(y, P, H, pair_index, weights, T, k, out, out_bf16, stream));
+}
+
+namespace {
+
+// Shape checks of the layout conversions.
+int check_pack(int64_t R, int64_t K, int block) {
+  if (block != 32 && block != 16) return SHARQ_EINVAL;
+  if (R < 0 || K <= 0 || K % 32 != 0) return SHARQ_EINVAL;
+  if (R >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if ((K + 127) / 128 * R * 64 >= ((int64_t)1 << 31)) return SHARQ_EINVAL;  // stage-major codes bytes
+  return SHARQ_OK;
+}
+
+}  // namespace
+
+int sharq_pack_stage_major(const uint8_t* codes_rm, const uint8_t* scales_rm, int64_t R, int64_t K, int block,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int rc = check_pack(R, K, block);
+  if (rc != SHARQ_OK) return rc;
+  if (R == 0) return SHARQ_OK;
+  if (!codes_rm || !scales_rm || !codes || !scales) return SHARQ_EINVAL;
+  if (!aligned16(codes_rm) || !aligned16(codes)) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_pack(codes_rm, scales_rm, R, K, block, codes, scales, stream));
+}
+
+int sharq_unpack_stage_major(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t K, int block,
+                             uint8_t* codes_rm, uint8_t* scales_rm, hipStream_t stream) {
+  const int rc = check_pack(R, K, block);
+  if (rc != SHARQ_OK) return rc;
+  if (R == 0) return SHARQ_OK;
+  if (!codes_rm || !scales_rm || !codes || !scales) return SHARQ_EINVAL;
+  if (!aligned16(codes_rm) || !aligned16(codes)) return SHARQ_EALIGN;
+  return hip_status(sharq::launch_unpack(codes, scales, R, K, block, codes_rm, scales_rm, stream));
 }
 
 int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream) {

@@ -76,6 +76,12 @@ hipError_t launch_linear_nvfp4(const uint8_t* bb_codes, const uint8_t* bb_scales
                                float s_w, int64_t T, int64_t O, int64_t K, float* y, int64_t ldy,
                                hipStream_t stream);
 
+hipError_t launch_pack(const uint8_t* codes_rm, const uint8_t* scales_rm, int64_t R, int64_t K, int block,
+                       uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_unpack(const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t K, int block,
+                         uint8_t* codes_rm, uint8_t* scales_rm, hipStream_t stream);
+
 hipError_t launch_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h, hipStream_t stream);
 
 }  // namespace sharq

@@ -356,6 +356,28 @@ SHARQ_API int sharq_silu_mul(const float* gu, int64_t T, int64_t I, uint16_t* h,
                    hipStream_t stream);
 
 /*
+ * sharq_pack_stage_major / sharq_unpack_stage_major -- layout conversion
+ * (data movement only) between the canonical row-major block-FP4 layout an
+ * external quantiser writes and the stage-major layout of every other entry
+ * point:
+ *   row-major:   codes u8 [R][K/2] (even K index in the low nibble),
+ *                scales u8 [R][K/block] (one byte per block of entries);
+ *   stage-major: codes u8 [G][R][64], scales u8 [G][R][128/block],
+ *                G = ceil(K/128), bytes past K zero (packing writes them).
+ * block is 32 (MXFP4, E8M0 scales) or 16 (NVFP4, E4M3 scales). Every code
+ * and scale byte is kept unchanged. Requires K % 32 == 0 and
+ * G * R * 64 < 2^31 (SHARQ_EINVAL otherwise); code pointers 16-byte aligned
+ * (scale pointers may have any alignment). Unpacking writes only the K/2
+ * code bytes and K/block scale bytes of each row.
+ */
+SHARQ_API int sharq_pack_stage_major(const uint8_t* codes_rm, const uint8_t* scales_rm,
+                           int64_t R, int64_t K, int block,
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream);
+SHARQ_API int sharq_unpack_stage_major(const uint8_t* codes, const uint8_t* scales,
+                             int64_t R, int64_t K, int block,
+                             uint8_t* codes_rm, uint8_t* scales_rm, hipStream_t stream);
+
+/*
  * NVFP4 (SharQ page, Abstract: the method generalises to NVFP4 as well as
  * MXFP4). The pages name NVFP4 without defining it; its public definition is
  * used: E2M1 codes in blocks of 16 consecutive K entries, one FP8 E4M3

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 7
+    assert _lib.call("sharq_abi_version") == 8
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
@@ -303,3 +303,20 @@ def test_nvfp4_validation():
     assert lin(K=48) == _lib.SHARQ_EINVAL
     assert lin(y=G + 4) == _lib.SHARQ_EALIGN
     assert lin(T=1 << 30, O=1 << 30) == _lib.SHARQ_EINVAL  # grid bound
+
+
+def test_pack_validation():
+    pk = lambda R=4, K=64, block=32, c=A, s=B, co=C, so=D: _lib.call(
+        "sharq_pack_stage_major", c, s, R, K, block, co, so, 0)
+    up = lambda R=4, K=64, block=32, c=A, s=B, co=C, so=D: _lib.call(
+        "sharq_unpack_stage_major", c, s, R, K, block, co, so, 0)
+    for f in (pk, up):
+        assert f(R=0) == _lib.SHARQ_OK
+        assert f(block=8) == _lib.SHARQ_EINVAL
+        assert f(K=48) == _lib.SHARQ_EINVAL
+        assert f(R=-1) == _lib.SHARQ_EINVAL
+        assert f(c=0) == _lib.SHARQ_EINVAL
+        assert f(c=A + 4) == _lib.SHARQ_EALIGN
+        assert f(co=C + 8) == _lib.SHARQ_EALIGN
+        assert f(R=1 << 24, K=1 << 12) == _lib.SHARQ_EINVAL  # stage-major bytes past 2^31
+        assert f(s=B + 1, so=D + 3, R=0) == _lib.SHARQ_OK       # scale pointers may be unaligned

@@ -63,7 +63,7 @@ typedef enum {
   SHARQ_EALIGN = -2,       /* pointer not 16-byte aligned, or ldx % 8 != 0 */
   SHARQ_EUNSUPPORTED = -3, /* (n, m) not in {(2,4), (8,16)} */
   SHARQ_EHIP = -4,         /* the HIP launch itself failed */
-  SHARQ_ENOTIMPL = -5      /* a shape class this build does not handle */
+  SHARQ_ENOTIMPL = -5      /* a shape class this library does not handle */
 } sharq_status;
 
 /* Host. Static string describing a status code; never NULL. */

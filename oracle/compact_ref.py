@@ -8,7 +8,7 @@ compression" inside the fused prepare without defining it; the 8:16 page
 2:4 and 0.875 for 8:16, which is ceil(log2 C(M, N)) bits per group of M:
 C(4, 2) = 6 patterns in 3 bits, C(16, 8) = 12870 patterns in 14 bits.
 
-Reading taken where they are silent (listed in the design doc):
+Reading taken where they are silent:
 * the compressed backbone of a row keeps, for every group of M, the N codes at
   the kept positions in index order (N/M of the dense nibbles), and one
   metadata field per group holding the rank of the kept position set;

@@ -15,8 +15,8 @@ used here is its public definition:
 * each tensor has one fp32 scale s_t on top, so that an entry decodes to
   e2m1(code) * e4m3(block scale) * s_t.
 
-Readings taken where the public description leaves steps open (each listed in
-the design doc), all arithmetic in fp32 with round-to-nearest-even unless stated:
+Readings taken where the public description leaves steps open, all
+arithmetic in fp32 with round-to-nearest-even unless stated:
 * block scale: v = amax_block / fp32(6 * s_t) (a correctly rounded division),
   then the E4M3 value nearest to v, ties to the even code, saturated to 448
   (never NaN); amax is over the entries being coded (the kept ones for the

@@ -33,7 +33,7 @@ Sources (cited by page title and section):
 * [8:16] "From 2:4 to 8:16 sparsity patterns in LLMs for Outliers and Weights
   with Variance Correction", key design: 8 of every 16 elements are kept.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   selection is on x' (after gamma); ties in |x'| go to the lower index; a group
   always keeps exactly N elements; scale blocks are 32 consecutive dense-K
   positions; an all-zero block gets exponent -127 (E8M0 byte 0x00); exponents

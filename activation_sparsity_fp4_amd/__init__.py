@@ -220,8 +220,9 @@ def _workspace(device, nbytes):
 
 def linear(prep: Prepared, w: MXFP4, out=None, split_k: bool = True):
     """Two-path FP4 GEMM: Y = deq(backbone) W^T + deq(residual) W^T, fp32 [T, O].
-    With split_k, problems with too few output tiles to fill the GPU split K
-    over a cached workspace (sharq_linear_ws); the result is deterministic."""
+    With split_k, K is split over a cached workspace (sharq_linear_ws) where
+    the library's plan expects it to be faster (too few output tiles to fill
+    the GPU, K long enough); the result is deterministic."""
     torch = _torch()
     _check_prepared(prep)
     _need(w.codes, torch.uint8, "w.codes", 3)
@@ -329,7 +330,7 @@ def _fused_call(prep, w_gu, T, I, K, n, m, h, hp, split_k):
             prep.res_scales.data_ptr(), w_gu.codes.data_ptr(), w_gu.scales.data_ptr(), T, I, K, n, m, _ptr(h),
             _ptr(hp and hp.bb_codes), _ptr(hp and hp.bb_scales), _ptr(hp and hp.res_codes),
             _ptr(hp and hp.res_scales), _ptr(hp and hp.mask))
-    nbytes = _lib.call("sharq_linear_workspace_bytes", T, 2 * I, K) if split_k else 0
+    nbytes = _lib.call("sharq_linear_silu_prepare_workspace_bytes", T, I, K) if split_k else 0
     if nbytes > 0:
         ws = _workspace(dev, nbytes)
         st = _lib.call("sharq_linear_silu_prepare_ws", *args, ws.data_ptr(), ws.numel(), _stream(dev))

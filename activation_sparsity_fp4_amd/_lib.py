@@ -39,6 +39,7 @@ SIGNATURES = {
                                   _I64, _P]),
     "sharq_linear": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "sharq_linear_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "sharq_linear_silu_prepare_workspace_bytes": (_I64, [_I64, _I64, _I64]),
     "sharq_linear_ws": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "sharq_linear_grouped": (_INT, [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _I64, _I64, _I64, _P,
                                     _P]),

@@ -45,6 +45,8 @@
 // accumulator's register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l % 32.
 
+#include <cmath>
+
 #include "prepare_block.h"
 #include "sharq_device.h"
 #include "sharq_internal.h"
@@ -678,12 +680,9 @@ __device__ __forceinline__ void store_tile(const v16f (&acc)[C::WM][C::WN], floa
 struct TileIndex {
   int tm, tn;
 };
-__device__ __forceinline__ TileIndex tile_index(int b, int tiles_m, int tiles_total) {
-  int tile = b;
-  if ((tiles_total & 7) == 0) {
-    const int per_xcd = tiles_total >> 3;
-    tile = (b & 7) * per_xcd + (b >> 3);
-  }
+// Tile t of tiles_total in walking order: groups of 4 row tiles walk the
+// column tiles with the row tiles innermost.
+__device__ __forceinline__ TileIndex tile_order(int tile, int tiles_m, int tiles_total) {
   constexpr int kGroup = 4;
   const int tiles_n = tiles_total / tiles_m;
   const int group = tile / (kGroup * tiles_n);
@@ -691,6 +690,17 @@ __device__ __forceinline__ TileIndex tile_index(int b, int tiles_m, int tiles_to
   const int gsize = min(tiles_m - first_m, kGroup);
   const int in_group = tile - group * kGroup * tiles_n;
   return TileIndex{first_m + in_group % gsize, in_group / gsize};
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs: block b of a grid
+// of n (n % 8 == 0) becomes item (b % 8) (n / 8) + b / 8, so that each XCD
+// takes a contiguous range of items.
+__device__ __forceinline__ int xcd_item(int b, int n) {
+  return (n & 7) == 0 ? (b & 7) * (n >> 3) + (b >> 3) : b;
+}
+
+__device__ __forceinline__ TileIndex tile_index(int b, int tiles_m, int tiles_total) {
+  return tile_order(xcd_item(b, tiles_total), tiles_m, tiles_total);
 }
 
 // LDS of the main loops: the ring's stages, or the general path's double buffer.
@@ -730,8 +740,11 @@ __global__ __launch_bounds__(C::kThreads, C::kOccupancy) void linear_split_kerne
                                                                               int tiles_m, int tiles_total, int S,
                                                                               float* __restrict__ partials) {
   SHARQ_GEMM_LDS(C, true)
-  const int split = blockIdx.x % S;
-  const TileIndex ti = tile_index(blockIdx.x / S, tiles_m, tiles_total);
+  // split-major items in XCD ranges: an XCD takes one or a few K slices of
+  // neighbouring tiles, so each weight slice is read into one L2
+  const int item = xcd_item(blockIdx.x, tiles_total * S);
+  const int split = item / tiles_total;
+  const TileIndex ti = tile_order(item - split * tiles_total, tiles_m, tiles_total);
   TileRows tr;
   tr.m0 = (int64_t)ti.tm * C::BM;
   tr.rows_valid = T - tr.m0 < C::BM ? T - tr.m0 : C::BM;
@@ -1092,8 +1105,6 @@ bool ring_path_ok(int64_t rows, int64_t O, int64_t K) {
   return K % 128 == 0 && rows * (K / 2) < lim && O * (K / 2) < lim;
 }
 
-// Tiles for two workgroups on each of MI355X's 256 CUs.
-constexpr int64_t kTwoPerCu = 512;
 // Problems with at least one tile per CU take the ring of 2 (which leaves LDS
 // for a second workgroup per CU); below that the ring of 4. At exactly one
 // tile per CU (the Llama-3.1-8B down projection) the ring of 2 measured 3%
@@ -1109,15 +1120,6 @@ void launch_tiles(const Operands& op, int64_t T, float* y, int64_t ldy, hipStrea
                      total);
 }
 
-// Split-K plan: problems with at most 256 rows and fewer 128 x 256 tiles
-// than two per CU (and K long enough) split K so that about two workgroups
-// per CU take part, each over at least 4 stages, at most 16 splits, and with
-// the partials (4 S T O bytes, written once and read once) at most the
-// larger of a quarter of the weight's bytes (O K 17/32) and 32 MB: a small
-// layer is latency-bound and gains from the parallelism even when the
-// partials outweigh its weight.
-constexpr int64_t kSplitMaxRows = 256;
-
 // The tile of a problem with T rows on the ring path: 0 SmallTile (or
 // DeepTile), 1 DecodeTile, 2 Decode64Tile.
 int row_tile(int64_t T) { return T <= DecodeTile::BM ? 1 : T <= Decode64Tile::BM ? 2 : 0; }
@@ -1132,21 +1134,56 @@ struct SplitPlan {
   int64_t partial_bytes;
 };
 
-SplitPlan split_plan(int64_t T, int64_t O, int64_t K) {
+// Split-K plan: the S in [1, 16] (each split over at least 4 stages, the
+// partials at most 256 MB) with the smallest estimated launch time. The
+// estimate was fitted to timed launches (S = 1 .. 16) of nine layer shapes
+// on MI355X, T = 1 .. 1024, O x K from 1024 x 8192 to 57344 x 8192:
+//  - the K loop: nsteps / S stages of c us (0.45 for the 32-row tile, 0.6
+//    for the 64-row one, 0.72 for the 128-row one) while a CU runs one
+//    workgroup; W = S * tiles workgroups put ceil(W / 256) on a CU, which
+//    runs them two at a time at 1.7 times the time of one;
+//  - no faster than streaming the weight and the activations (17/32 bytes
+//    per weight entry, 17/16 per activation entry: two paths) at 6.5 TB/s;
+//  - for S > 1, the partials: each split writes its fp32 tile and the
+//    reduce reads them all and writes Y, (2S + 1) T O 4 bytes at an
+//    effective 4 TB/s, plus 2 us for the second launch.
+// Long-K layers whose tiles leave CUs idle split (the Llama-3.1-8B down
+// projection at T = 384: 74 -> 34 us); wide layers that already fill the GPU
+// or stream their weight at the HBM rate do not (the Llama-3.1-70B gate|up at
+// T = 64: 71 us split in two, 48 us whole).
+constexpr int64_t kMaxPartialBytes = (int64_t)256 << 20;
+
+double split_cost_us(int64_t T, int64_t O, int64_t K, int tile, int64_t tiles, int64_t S) {
+  const int64_t nsteps = K / 128;
+  const double c = tile == 1 ? 0.45 : tile == 2 ? 0.6 : 0.72;
+  const int64_t per_cu = (S * tiles + 255) / 256;
+  const double crowd = per_cu <= 1 ? 1.0 : 1.7 * (double)per_cu / 2.0;
+  const double loop = (double)nsteps / (double)S * c * crowd;
+  const double stream = ((double)O * (double)K * 17.0 / 32.0 + (double)T * (double)K * 17.0 / 16.0) / 6.5e6;
+  double t = loop > stream ? loop : stream;
+  if (S > 1) t += 2.0 + (double)(2 * S + 1) * (double)T * (double)O * 4.0 / 4.0e6;
+  return t;
+}
+
+// fused: the plan of the fused gate|up entry. Its unsplit kernel has only
+// 128-row tiles; at decode-sized T (T <= 64) those run up to 128 times the
+// useful MFMA work with one workgroup per CU, so there the fused entry takes
+// the best split (the Llama-3.1-70B gate|up at T = 64: 70 us whole, 66 us in
+// two K slices).
+SplitPlan split_plan(int64_t T, int64_t O, int64_t K, bool fused) {
   SplitPlan p{1, 0, 0, 0, 0};
-  if (T <= 0 || T > kSplitMaxRows || O <= 0 || T * O >= ((int64_t)1 << 31) || !ring_path_ok(T, O, K)) return p;
+  if (T <= 0 || O <= 0 || T * O >= ((int64_t)1 << 31) || !ring_path_ok(T, O, K)) return p;
   p.tile = row_tile(T);
   const int64_t bm = row_tile_bm(p.tile);
   p.tiles_m = (int)((T + bm - 1) / bm);
   p.tiles_total = p.tiles_m * (int)((O + SmallTile::BN - 1) / SmallTile::BN);
-  const int64_t nsteps = K / 128;
-  int64_t S = kTwoPerCu / p.tiles_total;
-  S = S < nsteps / 4 ? S : nsteps / 4;
-  S = S < kMaxSplits ? S : kMaxSplits;
-  const int64_t w_bytes = O * K * 17 / 32;
-  const int64_t cap_bytes = w_bytes / 4 > ((int64_t)32 << 20) ? w_bytes / 4 : ((int64_t)32 << 20);
-  const int64_t traffic_cap = cap_bytes / (4 * T * O);
-  S = S < traffic_cap ? S : traffic_cap;
+  const int64_t s_max = K / 128 / 4 < kMaxSplits ? K / 128 / 4 : kMaxSplits;
+  int64_t S = 1;
+  double best = fused && p.tile != 0 ? HUGE_VAL : split_cost_us(T, O, K, p.tile, p.tiles_total, 1);
+  for (int64_t s = 2; s <= s_max && s * T * O * 4 <= kMaxPartialBytes; ++s) {
+    const double c = split_cost_us(T, O, K, p.tile, p.tiles_total, s);
+    if (c < best) best = c, S = s;
+  }
   if (S < 2) return p;
   p.S = (int)S;
   p.partial_bytes = S * T * O * 4;
@@ -1168,7 +1205,12 @@ void launch_split(const SplitPlan& p, const Operands& op, int64_t T, float* part
 }  // namespace
 
 int64_t linear_workspace_bytes(int64_t T, int64_t O, int64_t K) {
-  const SplitPlan p = split_plan(T, O, K);
+  const SplitPlan p = split_plan(T, O, K, false);
+  return p.S > 1 ? p.partial_bytes : 0;
+}
+
+int64_t linear_silu_prepare_workspace_bytes(int64_t T, int64_t I, int64_t K) {
+  const SplitPlan p = split_plan(T, 2 * I, K, true);
   return p.S > 1 ? p.partial_bytes : 0;
 }
 
@@ -1176,7 +1218,7 @@ hipError_t launch_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, c
                             const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,
                             int64_t O, int64_t K, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes,
                             hipStream_t stream) {
-  const SplitPlan p = split_plan(T, O, K);
+  const SplitPlan p = split_plan(T, O, K, false);
   if (p.S < 2 || !workspace || workspace_bytes < p.partial_bytes)
     return launch_linear(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K, y, ldy, stream);
   const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K);
@@ -1234,7 +1276,7 @@ hipError_t launch_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t*
                                          uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
                                          uint8_t* h_res_scales, uint8_t* h_mask, void* workspace,
                                          int64_t workspace_bytes, hipStream_t stream) {
-  const SplitPlan p = split_plan(T, 2 * I, K);
+  const SplitPlan p = split_plan(T, 2 * I, K, true);
   if (p.S < 2 || !workspace || workspace_bytes < p.partial_bytes)
     return launch_linear_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, I, K, n, m, h,
                                       h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, stream);

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 // Workgroups of one grouped launch: a one-dimensional grid of 256-thread
 // workgroups whose thread count must stay below 2^32.
 constexpr int64_t kMaxGroupedTiles = (int64_t)1 << 24;
@@ -243,6 +243,12 @@ int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb_scales,
   return hip_status(sharq::launch_linear_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales,
                                                       T, I, K, n, m, h, h_bb_codes, h_bb_scales, h_res_codes,
                                                       h_res_scales, h_mask, stream));
+}
+
+int64_t sharq_linear_silu_prepare_workspace_bytes(int64_t T, int64_t I, int64_t K) {
+  if (T <= 0 || I <= 0 || K <= 0 || I % 128 != 0 || K % 128 != 0) return 0;
+  if (T >= ((int64_t)1 << 31) || I >= ((int64_t)1 << 30) || K >= ((int64_t)1 << 31)) return 0;
+  return sharq::linear_silu_prepare_workspace_bytes(T, I, K);
 }
 
 int sharq_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,

@@ -20,6 +20,7 @@ hipError_t launch_linear(const uint8_t* bb_codes, const uint8_t* bb_scales, cons
                          int64_t T, int64_t O, int64_t K, float* y, int64_t ldy, hipStream_t stream);
 
 int64_t linear_workspace_bytes(int64_t T, int64_t O, int64_t K);
+int64_t linear_silu_prepare_workspace_bytes(int64_t T, int64_t I, int64_t K);
 
 hipError_t launch_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
                             const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,

@@ -152,13 +152,17 @@ SHARQ_API int sharq_linear(const uint8_t* bb_codes, const uint8_t* bb_scales,
  * sharq_linear_workspace_bytes -- host. Bytes of device workspace with which
  * sharq_linear_ws splits K for a (T, O, K) problem, or 0 when it would not
  * split (then sharq_linear_ws needs no workspace). Invalid shapes give 0.
+ * The split count is the one of 1 .. 16 with the smallest estimated launch
+ * time on MI355X (K loop, weight streaming, partials' traffic); it depends
+ * on the shape only.
  */
 SHARQ_API int64_t sharq_linear_workspace_bytes(int64_t T, int64_t O, int64_t K);
 
 /*
  * sharq_linear_ws -- sharq_linear (same arguments, same result up to the
  * accumulation order) that may split K across workgroups when the output has
- * too few tiles to fill the GPU (decode-sized T, small layers). Each split
+ * too few tiles to fill the GPU and K is long enough to pay for it (decode
+ * and mid-sized T, narrow layers). Each split
  * writes its fp32 partial tile into the workspace and a second kernel sums
  * the partials in split order, so calls are deterministic.
  *  workspace  device memory of at least sharq_linear_workspace_bytes(T, O, K)
@@ -229,20 +233,31 @@ SHARQ_API int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* 
                               hipStream_t stream);
 
 /*
- * sharq_linear_silu_prepare_ws -- sharq_linear_silu_prepare with the split-K
- * plan of sharq_linear_ws for problems with too few output tiles to fill the
- * GPU (decode-sized T): the gate|up GEMM stores fp32 partials over K slices
- * in `workspace`, and one more kernel sums them in slice order, forms h and
+ * sharq_linear_silu_prepare_workspace_bytes -- host. Bytes of device
+ * workspace with which sharq_linear_silu_prepare_ws splits K for a (T, I, K)
+ * problem (gate|up weight of 2 I rows), or 0 when it would not split. The
+ * plan is sharq_linear_workspace_bytes(T, 2 I, K)'s, except that the unsplit
+ * fused kernel has only 128-row tiles, so decode-sized T can split here
+ * where the plain GEMM would not. Invalid shapes give 0.
+ */
+SHARQ_API int64_t sharq_linear_silu_prepare_workspace_bytes(int64_t T, int64_t I, int64_t K);
+
+/*
+ * sharq_linear_silu_prepare_ws -- sharq_linear_silu_prepare that may split K
+ * across workgroups for problems with too few output tiles to fill the GPU
+ * (decode-sized T): the gate|up GEMM stores fp32 partials over K slices in
+ * `workspace`, and one more kernel sums them in slice order, forms h and
  * codes prepare(h) (glue and prepare as in sharq_linear_silu_prepare; the
  * method is the SharQ page's, Abstract and Section 1).
  *  arguments as sharq_linear_silu_prepare, plus
  *  workspace, workspace_bytes: caller-owned device memory of at least
- *              sharq_linear_workspace_bytes(T, 2 I, K) bytes, 16-byte
- *              aligned; contents need no initialisation and are overwritten.
- *              With a smaller (or NULL) workspace, or when that function
- *              returns 0, this is sharq_linear_silu_prepare.
- * Outputs are bit-identical to sharq_linear_ws + sharq_silu_mul +
- * sharq_prepare with the same workspace plan. Errors: as
+ *              sharq_linear_silu_prepare_workspace_bytes(T, I, K) bytes,
+ *              16-byte aligned; contents need no initialisation and are
+ *              overwritten. With a smaller (or NULL) workspace, or when that
+ *              function returns 0, this is sharq_linear_silu_prepare.
+ * When both workspace queries give the same size (the same split), outputs
+ * are bit-identical to sharq_linear_ws (T, 2 I, K) + sharq_silu_mul +
+ * sharq_prepare. Errors: as
  * sharq_linear_silu_prepare; workspace_bytes < 0, or > 0 with a NULL
  * workspace, is SHARQ_EINVAL; a misaligned workspace SHARQ_EALIGN.
  */

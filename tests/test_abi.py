@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 8
+    assert _lib.call("sharq_abi_version") == 9
     for s in (0, -1, -2, -3, -4, -5):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
@@ -172,12 +172,33 @@ def test_linear_workspace_bytes():
     assert ws(2048, 28672, 4096) == 0        # enough tiles: no split
     assert ws(8, 4096, 96) == 0              # K % 128 != 0: no split
     assert ws(4, 8, 48) == 0                 # invalid shape
-    # decode down projection: 32 column tiles, 16 splits of 14 stages, partials [16][1][8192] fp32
-    assert ws(1, 8192, 28672) == 16 * 1 * 8192 * 4
-    assert ws(64, 8192, 28672) == 16 * 64 * 8192 * 4
-    # 128 x 4096 layer: 16 tiles, 8 splits of 4 stages each
-    assert ws(128, 4096, 4096) == 8 * 128 * 4096 * 4
-    assert ws(300, 4096, 4096) == 0          # more rows than the split path takes
+    assert ws(1, 57344, 8192) == 0           # a weight this wide streams at the HBM rate unsplit
+    assert ws(1024, 4096, 4096) == 0         # short K: the partials would cost more than the idle CUs
+    # decode down projection 8192 x 28672: 6 splits, partials [6][1][8192] fp32
+    assert ws(1, 8192, 28672) == 6 * 1 * 8192 * 4
+    # Llama-3.1-8B down projection at T = 384 (48 tiles for 256 CUs): 5 splits
+    assert ws(384, 4096, 14336) == 5 * 384 * 4096 * 4
+    # every plan: S whole partials, 2 <= S <= 16, each split over at least 4 stages
+    for T in (1, 7, 32, 33, 64, 65, 130, 300, 777, 1024, 2048):
+        for O, K in ((1000, 8192), (4096, 4096), (8192, 28672), (1024, 512), (57344, 8192), (256, 131072)):
+            b = ws(T, O, K)
+            if b:
+                S = b // (T * O * 4)
+                assert b == S * T * O * 4 and 2 <= S <= min(16, K // 128 // 4), (T, O, K, S)
+
+
+def test_fused_workspace_bytes():
+    ws = lambda T, O, K: _lib.call("sharq_linear_workspace_bytes", T, O, K)
+    fw = lambda T, I, K: _lib.call("sharq_linear_silu_prepare_workspace_bytes", T, I, K)
+    assert fw(0, 128, 128) == 0 and fw(-1, 128, 128) == 0
+    assert fw(4, 96, 128) == 0 and fw(4, 128, 96) == 0   # I and K must be multiples of 128
+    assert fw(2048, 14336, 4096) == 0                     # enough tiles: no split
+    # Llama-3.1-70B decode gate|up: the plain GEMM runs it whole on 32-row tiles; the fused
+    # kernel has only 128-row tiles and splits K in two instead
+    assert ws(1, 57344, 8192) == 0 and fw(1, 28672, 8192) == 2 * 57344 * 4
+    # where the plain GEMM splits (T, 2 I, K), the fused entry splits the same way
+    for T, I, K in ((1, 1024, 4096), (5, 512, 2048), (64, 1024, 4096), (200, 512, 4096), (300, 512, 8192)):
+        assert fw(T, I, K) == ws(T, 2 * I, K) > 0, (T, I, K)
 
 
 def prep_rms(x=A, T=4, K=64, ldx=64, gamma=0, eps=1e-5, n=2, m=4, rms=G, bc=B, bs=C, rc=D, rs=E_, mask=F):

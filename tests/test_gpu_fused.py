@@ -95,8 +95,9 @@ def test_fused_split_k_matches_split_chain(sq, T, I, K, n, m):
     # prepares in one more kernel; the chain is linear (same split plan) -> silu_mul -> prepare
     import torch
     from activation_sparsity_fp4_amd import _lib
-    S_bytes = _lib.call("sharq_linear_workspace_bytes", T, 2 * I, K)
+    S_bytes = _lib.call("sharq_linear_silu_prepare_workspace_bytes", T, I, K)
     assert S_bytes > 0, "the shape must take the split-K path"
+    assert S_bytes == _lib.call("sharq_linear_workspace_bytes", T, 2 * I, K), "the chain must split the same way"
     print(f"fused split-K T={T} I={I} K={K} {n}:{m} workspace {S_bytes}", flush=True)
     x, w = _inputs(T, I, K, seed=7 * T + I + K)
     rows = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(3).choice(T, min(T, 16), replace=False)]))
@@ -104,17 +105,28 @@ def test_fused_split_k_matches_split_chain(sq, T, I, K, n, m):
 
 
 def test_fused_split_k_llama70b_decode_gate_up(sq):
-    # the Llama-3.1-70B decode gate|up at T = 1 (2 x 28672 outputs, K = 8192: two K slices); weights drawn
-    # on the GPU from a fixed seed (the reference is the GPU chain, itself checked against the oracle)
+    # the Llama-3.1-70B decode gate|up at T = 1 (2 x 28672 outputs, K = 8192): the plain GEMM runs it
+    # whole on 32-row tiles, the fused entry splits K in two. The chain repeats the two K slices as
+    # two whole GEMMs over the K halves (the same tile, each from zero, stages in order), adds them
+    # in slice order, gates and prepares: bit for bit. Weights drawn on the GPU from a fixed seed.
     import torch
+    from activation_sparsity_fp4_amd import _lib
     print("fused split-K llama70b decode gate|up T=1", flush=True)
     g = torch.Generator(device="cuda").manual_seed(70)
     I, K = 28672, 8192
+    assert _lib.call("sharq_linear_silu_prepare_workspace_bytes", 1, I, K) == 2 * 2 * I * 4, "two K slices"
     w = sq.quantize_mxfp4((torch.randn(2 * I, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16))
     rng = np.random.default_rng(70)
     x = bf16_round((rng.standard_normal((1, K)) * 2).astype(np.float32))
     p1 = sq.prepare(bf16_to_gpu(x), None, 2, 4)
-    y = sq.linear(p1, w)
+    G2 = p1.bb_codes.shape[0] // 2
+    halves = []
+    for sl in (slice(0, G2), slice(G2, None)):
+        ph = sq.Prepared(p1.bb_codes[sl].contiguous(), p1.bb_scales[sl].contiguous(), p1.res_codes[sl].contiguous(),
+                         p1.res_scales[sl].contiguous(), None, K // 2)
+        wh = sq.MXFP4(w.codes[sl].contiguous(), w.scales[sl].contiguous(), K // 2)
+        halves.append(sq.linear(ph, wh, split_k=False))
+    y = halves[0] + halves[1]
     h_ref = sq.silu_mul(y)
     p2_ref = sq.prepare(h_ref, None, 2, 4)
     hp, h = sq.linear_silu_prepare(p1, w, 2, 4, with_h=True)
@@ -124,4 +136,4 @@ def test_fused_split_k_llama70b_decode_gate_up(sq):
         assert np.array_equal(to_np(getattr(hp, f)), to_np(getattr(p2_ref, f))), f
     h_np = to_np(h)
     assert_prepare_equal(hp, prepare_ref(h_np, None, 2, 4))
-    assert_bf16_close(h_np, silu_mul_ref(to_np(y), I))
+    assert_bf16_close(h_np, silu_mul_ref(to_np(sq.linear(p1, w)), I))

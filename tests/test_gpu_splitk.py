@@ -1,5 +1,7 @@
 """GPU parity of the split-K two-path GEMM (sharq_linear_ws) used for problems
-with few output tiles: against the oracle's fp64 product to the GEMM
+with too few output tiles to fill the GPU: decode-sized T and, for long K,
+mid-sized T (several 128-row tiles, ragged rows and columns, split counts that
+are not powers of two). Against the oracle's fp64 product to the GEMM
 tolerance, bitwise repeatable, and with one workspace reused across shapes."""
 
 import numpy as np
@@ -32,7 +34,7 @@ def _problem(T, O, K, seed):
 
 
 @pytest.mark.parametrize("T,O,K", [(1, 8192, 4096), (5, 1000, 2048), (64, 2048, 8192), (12, 700, 3072),
-                                   (3, 4096, 8192)])
+                                   (3, 4096, 8192), (300, 1024, 4096), (500, 1000, 8192), (130, 3000, 4096)])
 def test_split_k_matches_oracle_and_repeats(sq, T, O, K):
     from activation_sparsity_fp4_amd import _lib
     print(f"split-K T={T} O={O} K={K}", flush=True)

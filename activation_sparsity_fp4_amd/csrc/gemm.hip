@@ -45,8 +45,6 @@
 // accumulator's register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l % 32.
 
-#include <cmath>
-
 #include "prepare_block.h"
 #include "sharq_device.h"
 #include "sharq_internal.h"
@@ -914,26 +912,28 @@ struct HOutputs {
 
 constexpr int kHStride = 272;  // bytes per h row in LDS: 256 + 16 keeps row starts on distinct banks
 
-// The tile's h = bf16(silu(gate) * up) (128 rows x 128 h columns) goes
+// The tile's h = bf16(silu(gate) * up) (BM rows x 128 h columns) goes
 // through LDS so that each lane then owns whole 32-entry blocks of h rows:
-// 512 (row, block) pairs, two per lane, each coded by the same per-block
-// prepare arithmetic as the prepare kernel.
-template <int N, int M>
-__device__ __forceinline__ void silu_prepare_epilogue(const v16f (&acc)[2][4], uint8_t* lds, const TileRows& tr,
-                                                      int64_t h0, const HOutputs& out) {
+// 4 BM (row, block) pairs, each coded by the same per-block prepare
+// arithmetic as the prepare kernel. A wave's four 32-column MFMA tiles are
+// gate, gate, up, up of 64 h columns (TileCols).
+template <class C, int N, int M>
+__device__ __forceinline__ void silu_prepare_epilogue(const v16f (&acc)[C::WM][C::WN], uint8_t* lds,
+                                                      const TileRows& tr, int64_t h0, const HOutputs& out) {
+  static_assert(C::WN == 4, "gate, gate, up, up column tiles per wave");
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % C::NWM, wn = wave / C::NWM;
   const int lr = lane & 31, lh = lane >> 5;
   ring_barrier();  // every wave is done with the ring before it is overwritten
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::WM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = 64 * wn + 32 * j + lr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int row = 32 * C::WM * wm + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
         const uint32_t hb = bf16_rne_bits(silu_times(acc[i][j][r], acc[i][j + 2][r]));
         *reinterpret_cast<uint16_t*>(lds + row * kHStride + 2 * col) = (uint16_t)hb;
       }
@@ -941,10 +941,10 @@ __device__ __forceinline__ void silu_prepare_epilogue(const v16f (&acc)[2][4], u
   __syncthreads();
   const int64_t blk0 = h0 >> 5;  // first 32-block of the tile along I
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int p = tid + 256 * k;
+  for (int k = 0; k < (4 * C::BM + C::kThreads - 1) / C::kThreads; ++k) {
+    const int p = tid + C::kThreads * k;
     const int row = p >> 2, blk = p & 3;
-    if (row >= tr.rows_valid) continue;
+    if (row >= C::BM || row >= tr.rows_valid) continue;
     const int64_t t = tr.m0 + row;
     const uint4* src = reinterpret_cast<const uint4*>(lds + row * kHStride + 64 * blk);
     uint4 raw[4];
@@ -980,10 +980,11 @@ __device__ __forceinline__ void silu_prepare_epilogue(const v16f (&acc)[2][4], u
 // One 128 x 128 h tile: the two-path GEMM over the tile's 128 gate and 128 up
 // weight rows, then the fused epilogue.
 template <class C, int N, int M>
-__global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_kernel(Operands op, HOutputs out,
-                                                                                      int tiles_m, int tiles_total) {
-  static_assert(C::WM == 2 && C::WN == 4 && C::NWM == 2, "the epilogue assumes 128 x 256 tiles of 2 x 2 waves");
-  static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
+__global__ __launch_bounds__(C::kThreads, C::kOccupancy) void linear_silu_prepare_kernel(Operands op, HOutputs out,
+                                                                                         int tiles_m,
+                                                                                         int tiles_total) {
+  static_assert(C::BN == 256, "one tile covers 128 h columns");
+  static_assert(C::kRing * C::kStage >= C::BM * kHStride, "the h tile must fit in the ring's LDS");
   SHARQ_GEMM_LDS(C, true)
   const TileIndex ti = tile_index(blockIdx.x, tiles_m, tiles_total);
   const int tm = ti.tm, tn = ti.tn;
@@ -995,7 +996,7 @@ __global__ __launch_bounds__(kThreads, C::kOccupancy) void linear_silu_prepare_k
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   mainloop_ring<C>(op, tr, TileCols{h0, out.I}, lds, acc, 0, op.nsteps);
-  silu_prepare_epilogue<N, M>(acc, lds, tr, h0, out);
+  silu_prepare_epilogue<C, N, M>(acc, lds, tr, h0, out);
 }
 
 // Split-K form of the fused gate|up epilogue, for problems with too few
@@ -1079,7 +1080,7 @@ __global__ __launch_bounds__(kThreads, SmallTile::kOccupancy) void linear_groupe
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
   mainloop_ring<C, true>(op, g.tr, TileCols{h0, out.I}, lds, acc, 0, op.nsteps);
-  silu_prepare_epilogue<N, M>(acc, lds, g.tr, h0, out);
+  silu_prepare_epilogue<C, N, M>(acc, lds, g.tr, h0, out);
 }
 
 Operands make_operands(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
@@ -1165,12 +1166,7 @@ double split_cost_us(int64_t T, int64_t O, int64_t K, int tile, int64_t tiles, i
   return t;
 }
 
-// fused: the plan of the fused gate|up entry. Its unsplit kernel has only
-// 128-row tiles; at decode-sized T (T <= 64) those run up to 128 times the
-// useful MFMA work with one workgroup per CU, so there the fused entry takes
-// the best split (the Llama-3.1-70B gate|up at T = 64: 70 us whole, 66 us in
-// two K slices).
-SplitPlan split_plan(int64_t T, int64_t O, int64_t K, bool fused) {
+SplitPlan split_plan(int64_t T, int64_t O, int64_t K) {
   SplitPlan p{1, 0, 0, 0, 0};
   if (T <= 0 || O <= 0 || T * O >= ((int64_t)1 << 31) || !ring_path_ok(T, O, K)) return p;
   p.tile = row_tile(T);
@@ -1179,7 +1175,7 @@ SplitPlan split_plan(int64_t T, int64_t O, int64_t K, bool fused) {
   p.tiles_total = p.tiles_m * (int)((O + SmallTile::BN - 1) / SmallTile::BN);
   const int64_t s_max = K / 128 / 4 < kMaxSplits ? K / 128 / 4 : kMaxSplits;
   int64_t S = 1;
-  double best = fused && p.tile != 0 ? HUGE_VAL : split_cost_us(T, O, K, p.tile, p.tiles_total, 1);
+  double best = split_cost_us(T, O, K, p.tile, p.tiles_total, 1);
   for (int64_t s = 2; s <= s_max && s * T * O * 4 <= kMaxPartialBytes; ++s) {
     const double c = split_cost_us(T, O, K, p.tile, p.tiles_total, s);
     if (c < best) best = c, S = s;
@@ -1205,12 +1201,12 @@ void launch_split(const SplitPlan& p, const Operands& op, int64_t T, float* part
 }  // namespace
 
 int64_t linear_workspace_bytes(int64_t T, int64_t O, int64_t K) {
-  const SplitPlan p = split_plan(T, O, K, false);
+  const SplitPlan p = split_plan(T, O, K);
   return p.S > 1 ? p.partial_bytes : 0;
 }
 
 int64_t linear_silu_prepare_workspace_bytes(int64_t T, int64_t I, int64_t K) {
-  const SplitPlan p = split_plan(T, 2 * I, K, true);
+  const SplitPlan p = split_plan(T, 2 * I, K);
   return p.S > 1 ? p.partial_bytes : 0;
 }
 
@@ -1218,7 +1214,7 @@ hipError_t launch_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, c
                             const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,
                             int64_t O, int64_t K, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes,
                             hipStream_t stream) {
-  const SplitPlan p = split_plan(T, O, K, false);
+  const SplitPlan p = split_plan(T, O, K);
   if (p.S < 2 || !workspace || workspace_bytes < p.partial_bytes)
     return launch_linear(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K, y, ldy, stream);
   const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, O, K);
@@ -1276,7 +1272,7 @@ hipError_t launch_linear_silu_prepare_ws(const uint8_t* bb_codes, const uint8_t*
                                          uint8_t* h_bb_codes, uint8_t* h_bb_scales, uint8_t* h_res_codes,
                                          uint8_t* h_res_scales, uint8_t* h_mask, void* workspace,
                                          int64_t workspace_bytes, hipStream_t stream) {
-  const SplitPlan p = split_plan(T, 2 * I, K, true);
+  const SplitPlan p = split_plan(T, 2 * I, K);
   if (p.S < 2 || !workspace || workspace_bytes < p.partial_bytes)
     return launch_linear_silu_prepare(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, I, K, n, m, h,
                                       h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, stream);
@@ -1302,17 +1298,25 @@ hipError_t launch_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* bb
                                       uint8_t* h_res_scales, uint8_t* h_mask, hipStream_t stream) {
   const Operands op = make_operands(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales, T, 2 * I, K);
   const HOutputs out{h, h_bb_codes, h_bb_scales, h_res_codes, h_res_scales, h_mask, T, I};
-  const int tiles_m = (int)((T + 127) / 128);
+  const int tile = row_tile(T);
+  const int64_t bm = row_tile_bm(tile);
+  const int tiles_m = (int)((T + bm - 1) / bm);
   const int total = tiles_m * (int)(I / 128);
   const bool two = total >= kSmallTileMin;
-#define SHARQ_FUSED(C, NN, MM)                                                                                    \
-  hipLaunchKernelGGL((linear_silu_prepare_kernel<C, NN, MM>), dim3(total), dim3(kThreads), 0, stream, op, out, \
+#define SHARQ_FUSED(C, NN, MM)                                                                                       \
+  hipLaunchKernelGGL((linear_silu_prepare_kernel<C, NN, MM>), dim3(total), dim3(C::kThreads), 0, stream, op, out, \
                      tiles_m, total)
+#define SHARQ_FUSED_NM(NN, MM)                        \
+  if (tile == 1) SHARQ_FUSED(DecodeTile, NN, MM);     \
+  else if (tile == 2) SHARQ_FUSED(Decode64Tile, NN, MM); \
+  else if (two) SHARQ_FUSED(SmallTile, NN, MM);       \
+  else SHARQ_FUSED(DeepTile, NN, MM)
   if (n == 2 && m == 4) {
-    if (two) SHARQ_FUSED(SmallTile, 2, 4); else SHARQ_FUSED(DeepTile, 2, 4);
+    SHARQ_FUSED_NM(2, 4);
   } else {
-    if (two) SHARQ_FUSED(SmallTile, 8, 16); else SHARQ_FUSED(DeepTile, 8, 16);
+    SHARQ_FUSED_NM(8, 16);
   }
+#undef SHARQ_FUSED_NM
 #undef SHARQ_FUSED
   return hipGetLastError();
 }

@@ -235,10 +235,10 @@ SHARQ_API int sharq_linear_silu_prepare(const uint8_t* bb_codes, const uint8_t* 
 /*
  * sharq_linear_silu_prepare_workspace_bytes -- host. Bytes of device
  * workspace with which sharq_linear_silu_prepare_ws splits K for a (T, I, K)
- * problem (gate|up weight of 2 I rows), or 0 when it would not split. The
- * plan is sharq_linear_workspace_bytes(T, 2 I, K)'s, except that the unsplit
- * fused kernel has only 128-row tiles, so decode-sized T can split here
- * where the plain GEMM would not. Invalid shapes give 0.
+ * problem (gate|up weight of 2 I rows), or 0 when it would not split: the
+ * plan of sharq_linear_workspace_bytes(T, 2 I, K) (the fused kernel has the
+ * plain GEMM's row tiles, the 32- and 64-row decode tiles included). Invalid
+ * shapes give 0.
  */
 SHARQ_API int64_t sharq_linear_silu_prepare_workspace_bytes(int64_t T, int64_t I, int64_t K);
 
@@ -255,9 +255,8 @@ SHARQ_API int64_t sharq_linear_silu_prepare_workspace_bytes(int64_t T, int64_t I
  *              16-byte aligned; contents need no initialisation and are
  *              overwritten. With a smaller (or NULL) workspace, or when that
  *              function returns 0, this is sharq_linear_silu_prepare.
- * When both workspace queries give the same size (the same split), outputs
- * are bit-identical to sharq_linear_ws (T, 2 I, K) + sharq_silu_mul +
- * sharq_prepare. Errors: as
+ * Outputs are bit-identical to sharq_linear_ws (T, 2 I, K) + sharq_silu_mul
+ * + sharq_prepare (the same split plan). Errors: as
  * sharq_linear_silu_prepare; workspace_bytes < 0, or > 0 with a NULL
  * workspace, is SHARQ_EINVAL; a misaligned workspace SHARQ_EALIGN.
  */

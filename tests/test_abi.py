@@ -193,12 +193,12 @@ def test_fused_workspace_bytes():
     assert fw(0, 128, 128) == 0 and fw(-1, 128, 128) == 0
     assert fw(4, 96, 128) == 0 and fw(4, 128, 96) == 0   # I and K must be multiples of 128
     assert fw(2048, 14336, 4096) == 0                     # enough tiles: no split
-    # Llama-3.1-70B decode gate|up: the plain GEMM runs it whole on 32-row tiles; the fused
-    # kernel has only 128-row tiles and splits K in two instead
-    assert ws(1, 57344, 8192) == 0 and fw(1, 28672, 8192) == 2 * 57344 * 4
-    # where the plain GEMM splits (T, 2 I, K), the fused entry splits the same way
-    for T, I, K in ((1, 1024, 4096), (5, 512, 2048), (64, 1024, 4096), (200, 512, 4096), (300, 512, 8192)):
-        assert fw(T, I, K) == ws(T, 2 * I, K) > 0, (T, I, K)
+    # the fused entry splits exactly as the plain GEMM over (T, 2 I, K)
+    assert fw(1, 28672, 8192) == ws(1, 57344, 8192) == 0   # Llama-3.1-70B decode gate|up: whole
+    for T, I, K in ((1, 1024, 4096), (5, 512, 2048), (64, 1024, 4096), (200, 512, 4096), (300, 512, 8192),
+                    (1, 14336, 4096), (20, 14336, 4096), (50, 2048, 1024)):
+        assert fw(T, I, K) == ws(T, 2 * I, K), (T, I, K)
+    assert fw(200, 512, 4096) > 0
 
 
 def prep_rms(x=A, T=4, K=64, ldx=64, gamma=0, eps=1e-5, n=2, m=4, rms=G, bc=B, bs=C, rc=D, rs=E_, mask=F):

@@ -726,10 +726,11 @@ __global__ __launch_bounds__(C::kThreads, kRingPath ? C::kOccupancy : 1) void li
   store_tile<C>(acc, y, ldy, tr.m0, tr.rows_valid, n0, op.O);
 }
 
-// Split-K two-path GEMM for problems with few output tiles (decode-sized T,
-// small layers). Workgroup b computes split b % S (stages [S0, S1) of K,
-// S0 = split * nsteps / S) of tile b / S and stores its fp32 partial tile in
-// partials[split] ([S][T][O]); split_reduce_kernel then sums the partials in
+// Split-K two-path GEMM for problems with too few output tiles to fill the
+// GPU and a long enough K (split_plan). Item q of the S * tiles work items
+// (numbered in XCD ranges) computes split q / tiles (stages [S0, S1) of K,
+// S0 = split * nsteps / S) of tile q % tiles and stores its fp32 partial tile
+// in partials[split] ([S][T][O]); split_reduce_kernel then sums the partials in
 // split order 0, 1, ..., S-1, so the result does not depend on timing. The
 // kernel boundary between the two launches makes the partials visible to
 // every XCD.
@@ -999,8 +1000,8 @@ __global__ __launch_bounds__(C::kThreads, C::kOccupancy) void linear_silu_prepar
   silu_prepare_epilogue<C, N, M>(acc, lds, tr, h0, out);
 }
 
-// Split-K form of the fused gate|up epilogue, for problems with too few
-// tiles to fill the GPU (decode-sized T). linear_split_kernel has stored the
+// Split-K form of the fused gate|up epilogue, for problems that the split
+// plan splits (too few tiles to fill the GPU, long K). linear_split_kernel has stored the
 // partials [S][T][2I] of the plain gate|up GEMM; here lane (t, b) owns the
 // 32-entry h block b of row t (a wave: a 16-row band of one 128-entry stage,
 // as in the prepare kernel), sums the S partials of its 32 gate and 32 up

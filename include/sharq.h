@@ -244,8 +244,8 @@ SHARQ_API int64_t sharq_linear_silu_prepare_workspace_bytes(int64_t T, int64_t I
 
 /*
  * sharq_linear_silu_prepare_ws -- sharq_linear_silu_prepare that may split K
- * across workgroups for problems with too few output tiles to fill the GPU
- * (decode-sized T): the gate|up GEMM stores fp32 partials over K slices in
+ * across workgroups where its plan splits (too few output tiles to fill the
+ * GPU, K long enough): the gate|up GEMM stores fp32 partials over K slices in
  * `workspace`, and one more kernel sums them in slice order, forms h and
  * codes prepare(h) (glue and prepare as in sharq_linear_silu_prepare; the
  * method is the SharQ page's, Abstract and Section 1).

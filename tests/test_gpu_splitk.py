@@ -34,7 +34,8 @@ def _problem(T, O, K, seed):
 
 
 @pytest.mark.parametrize("T,O,K", [(1, 8192, 4096), (5, 1000, 2048), (64, 2048, 8192), (12, 700, 3072),
-                                   (3, 4096, 8192), (300, 1024, 4096), (500, 1000, 8192), (130, 3000, 4096)])
+                                   (3, 4096, 8192), (300, 1024, 4096), (500, 1000, 8192), (130, 3000, 4096),
+                                   (65, 2048, 8192), (257, 1024, 8192)])
 def test_split_k_matches_oracle_and_repeats(sq, T, O, K):
     from activation_sparsity_fp4_amd import _lib
     print(f"split-K T={T} O={O} K={K}", flush=True)

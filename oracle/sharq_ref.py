@@ -44,8 +44,8 @@ Readings where the pages are silent:
 Parity pins (tests/test_oracle_*.py): every public function below is pinned
 against something other than itself -- brute-force enumeration, exhaustive
 sweeps against numpy's own half-to-even rounding, closed forms and exact
-invariants. ``silu_mul_ref`` is pinned only by closed-form points and
-monotonicity checks (its transcendental has no exact reference here).
+invariants. ``silu_mul_ref`` is pinned against a 50-digit mpmath evaluation
+of silu(g) * u rounded to bf16 by an independent midpoint search.
 """
 
 from __future__ import annotations
@@ -103,39 +103,29 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
 
 
 def f64_to_bf16_bits_rne(h: np.ndarray) -> np.ndarray:
-    """Round float64 values to bf16 (8-bit significand) to nearest, ties to even.
+    """Round float64 values to the nearest bf16, ties to the even significand.
 
-    Done in one rounding step from the float64 value: m * 2**ex with m in [0.5, 1)
-    is rounded to 8 significant bits with numpy's half-to-even ``rint``. Results
-    are normal-range bf16 values (the values this is used for never reach the
-    bf16 subnormal range) or zero.
+    Written from the bf16 grid: in the binade of h (exponent e = floor(log2|h|))
+    bf16 values are spaced 2**(e - 7), and below 2**-126 (the subnormal range)
+    uniformly 2**-133; h / spacing is rounded half-to-even by numpy's ``rint``
+    in one step from the float64 value and scaled back exactly. Finite inputs
+    whose rounding stays finite in bf16 only.
     """
     h = np.asarray(h, dtype=np.float64)
     _require_finite(h, "f64_to_bf16_bits_rne")
-    m, ex = np.frexp(h)
-    r = np.ldexp(np.rint(np.ldexp(m, 8)), ex - 8)  # exact in float64
-    r32 = r.astype(np.float32)  # exact: r has 8 significant bits
+    a = np.abs(h)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))  # a = f * 2**ex, f in [0.5, 1): e = ex - 1
+    step_exp = np.maximum(ex - 1 - 7, -133)
+    r = np.ldexp(np.rint(np.ldexp(h, -step_exp)), step_exp)  # exact in float64
+    r32 = r.astype(np.float32)  # exact: r lies on the bf16 grid
+    _require_finite(r32, "bf16 rounding")
     return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def f32_to_bf16_bits_rne(v32: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bf16, ties to the even significand.
-
-    Written from the bf16 grid: in the binade of v (exponent e = floor(log2|v|))
-    bf16 values are spaced 2**(e - 7), and below 2**-126 (the subnormal range)
-    uniformly 2**-133; v / spacing is rounded half-to-even by numpy's ``rint``
-    and scaled back, exactly, in float64. Finite inputs whose rounding stays
-    finite in bf16 only.
-    """
-    v = np.asarray(v32, dtype=np.float32).astype(np.float64)
-    _require_finite(v, "f32_to_bf16_bits_rne")
-    a = np.abs(v)
-    _, ex = np.frexp(np.where(a > 0, a, 1.0))  # a = f * 2**ex, f in [0.5, 1): e = ex - 1
-    step_exp = np.maximum(ex - 1 - 7, -133)
-    r = np.ldexp(np.rint(np.ldexp(v, -step_exp)), step_exp)
-    r32 = r.astype(np.float32)  # exact: r lies on the bf16 grid
-    _require_finite(r32, "bf16 rounding")
-    return (r32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    """Round float32 values to the nearest bf16, ties to the even significand
+    (float32 -> float64 is exact, then the bf16 grid rounding above)."""
+    return f64_to_bf16_bits_rne(np.asarray(v32, dtype=np.float32).astype(np.float64))
 
 
 # ---------------------------------------------------------------------------

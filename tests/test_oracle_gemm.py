@@ -120,3 +120,61 @@ def test_bf16_rounding_ties_to_even():
     # 1 + 3 * 2**-8 is halfway between 1 + 2**-7 and 1 + 2**-6: goes to 1 + 2**-6 (even)
     assert f64_to_bf16_bits_rne(np.array([1 + 3 * 2.0 ** -8]))[0] == 0x3F82
     assert f64_to_bf16_bits_rne(np.array([-0.0]))[0] == 0x8000
+
+
+def _mp_bf16_bits(v, zero_sign=False):
+    """The bf16 nearest to the mpmath value v (ties to the even significand),
+    found by bracketing v between adjacent bf16 values of its binade and
+    comparing against their midpoint in mpmath arithmetic. mpmath has no
+    signed zero: an exact zero takes the sign `zero_sign` (IEEE's sign rule
+    for the operation that produced it)."""
+    import mpmath
+    if v == 0:
+        return 0x8000 if zero_sign else 0
+    neg = v < 0
+    a = -v if neg else v
+    m, ex = mpmath.frexp(a)            # a = m * 2**ex, m in [0.5, 1)
+    step = max(int(ex) - 1 - 7, -133)  # bf16 spacing in this binade (subnormal grid below 2**-126)
+    q = a / mpmath.mpf(2) ** step
+    lo = int(mpmath.floor(q))
+    mid = mpmath.mpf(lo) + mpmath.mpf(1) / 2
+    n = lo + 1 if q > mid else lo if q < mid else (lo if lo % 2 == 0 else lo + 1)
+    r = np.float32(float(mpmath.mpf(n) * mpmath.mpf(2) ** step))  # exact: n has at most 9 bits
+    bits = int(r.view(np.uint32)) >> 16
+    return bits | (0x8000 if neg else 0)
+
+
+def test_silu_mul_against_mpmath():
+    """silu_mul_ref on float32 (g, u) pairs equals silu(g) * u evaluated with 50
+    significant digits and rounded to bf16 by a midpoint search, including
+    |g| >= 80 (results in bf16's subnormal range and exact zeros) and ties."""
+    import mpmath
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(7)
+    g = np.concatenate([rng.standard_normal(2000) * 3, rng.uniform(-120, -80, 300), rng.uniform(80, 120, 300),
+                        rng.uniform(-20, 20, 400), [0.0, -0.0, 1.0, -1.0, 88.5, -88.5, -103.0]]).astype(np.float32)
+    u = np.concatenate([rng.standard_normal(2000) * 2, rng.uniform(-1e3, 1e3, 300), rng.standard_normal(300),
+                        rng.standard_normal(400) * 1e-3, [1.0, 2.0, 3.0, -1.0, 1.0, 1e30, 1e30]]).astype(np.float32)
+    I = len(g)
+    got = silu_mul_ref(np.concatenate([g, u])[None, :], I)[0]
+    want = []
+    for gi, ui in zip(g.astype(np.float64), u.astype(np.float64)):
+        G, U = mpmath.mpf(gi), mpmath.mpf(ui)
+        # silu(+-0) = +-0 / 2, and a product of zeros carries the xor of the signs
+        want.append(_mp_bf16_bits(G / (1 + mpmath.exp(-G)) * U, bool(np.signbit(gi) ^ np.signbit(ui))))
+    want = np.array(want, dtype=np.uint16)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} mismatches, first g={g[bad[0]]} u={u[bad[0]]}: {got[bad[0]]:#06x} " \
+                          f"vs {want[bad[0]]:#06x}"
+    # the sample reaches the subnormal range and the signed zeros
+    assert np.any((want & 0x7F80) == 0) and np.any(want == 0x8000)
+
+
+def test_bf16_rounding_subnormal_grid():
+    """Below 2**-126 bf16 values are spaced 2**-133: the rounding stays on that grid."""
+    tiny = 2.0 ** -133
+    assert f64_to_bf16_bits_rne(np.array([tiny]))[0] == 0x0001
+    assert f64_to_bf16_bits_rne(np.array([0.5 * tiny]))[0] == 0x0000          # tie -> even (zero)
+    assert f64_to_bf16_bits_rne(np.array([1.5 * tiny]))[0] == 0x0002          # tie -> even
+    assert f64_to_bf16_bits_rne(np.array([-2.4 * tiny]))[0] == 0x8002
+    assert f64_to_bf16_bits_rne(np.array([127.5 * tiny]))[0] == 0x0080        # tie -> 128 = 2**-126 (normal)

@@ -142,6 +142,8 @@ def prepare(x, gamma=None, n: int = 2, m: int = 4, with_mask: bool = True, out: 
     T, K = x.shape
     if gamma is not None:
         _need(gamma, torch.bfloat16, "gamma", 1)
+        if gamma.numel() != K:  # the kernels read K entries of gamma
+            raise ValueError(f"gamma must hold K = {K} entries, got {gamma.numel()}")
         gamma = gamma.contiguous()
     if out is None:
         kw = dict(dtype=torch.uint8, device=x.device)
@@ -534,6 +536,8 @@ def prepare_nvfp4(x, tensor_scale: float, gamma=None, n: int = 2, m: int = 4, wi
     T, K = x.shape
     if gamma is not None:
         _need(gamma, torch.bfloat16, "gamma", 1)
+        if gamma.numel() != K:  # the kernels read K entries of gamma
+            raise ValueError(f"gamma must hold K = {K} entries, got {gamma.numel()}")
         gamma = gamma.contiguous()
     if out is None:
         kw = dict(dtype=torch.uint8, device=x.device)

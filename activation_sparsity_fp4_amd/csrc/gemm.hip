@@ -130,15 +130,21 @@ struct Operands {
   int nsteps;
 };
 
-// Row sources of one output tile: which activation row feeds tile row r, or -1.
+// Row sources of one output tile: which activation row feeds tile row r, or
+// -1 (the row then reads as zeros). A gathered index outside [0, src_rows)
+// is -1 as well, so malformed gather contents never address memory outside
+// the activation buffers.
 struct TileRows {
   int64_t m0;          // first output row of the tile
   int64_t rows_valid;  // output rows of the tile that exist (<= the tile height)
   const int32_t* gather;  // activation row of each output row, or nullptr (identity)
+  int64_t src_rows;    // rows of the activation buffers (bound of a gathered index)
   __device__ __forceinline__ int64_t src(int r) const {
     if (r >= rows_valid) return -1;
     const int64_t p = m0 + r;
-    return gather ? (int64_t)gather[p] : p;
+    if (!gather) return p;
+    const int64_t g = gather[p];
+    return g >= 0 && g < src_rows ? g : -1;
   }
 };
 
@@ -716,6 +722,7 @@ __global__ __launch_bounds__(C::kThreads, kRingPath ? C::kOccupancy : 1) void li
   tr.m0 = (int64_t)tm * C::BM;
   tr.rows_valid = T - tr.m0 < C::BM ? T - tr.m0 : C::BM;
   tr.gather = nullptr;
+  tr.src_rows = T;
   const int64_t n0 = (int64_t)tn * C::BN;
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
@@ -748,6 +755,7 @@ __global__ __launch_bounds__(C::kThreads, C::kOccupancy) void linear_split_kerne
   tr.m0 = (int64_t)ti.tm * C::BM;
   tr.rows_valid = T - tr.m0 < C::BM ? T - tr.m0 : C::BM;
   tr.gather = nullptr;
+  tr.src_rows = T;
   const int64_t n0 = (int64_t)ti.tn * C::BN;
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
@@ -815,7 +823,8 @@ __device__ __forceinline__ int expert_row_tiles(const int32_t* __restrict__ seg,
 
 template <class C, bool kXcdRanges>
 __device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ seg, int E, int64_t P,
-                                                    const int32_t* __restrict__ a_rows, int tiles_n) {
+                                                    const int32_t* __restrict__ a_rows, int64_t src_rows,
+                                                    int tiles_n) {
   __shared__ int s_info[3];
   const int tid = threadIdx.x;
   if (tid == 0) s_info[0] = -1;
@@ -862,6 +871,7 @@ __device__ __forceinline__ GroupedTile grouped_tile(const int32_t* __restrict__ 
     const int64_t hi = seg_bound(seg, g.e + 1, lo, P);
     g.tr.rows_valid = hi - g.tr.m0 < C::BM ? hi - g.tr.m0 : C::BM;
     g.tr.gather = a_rows;
+    g.tr.src_rows = src_rows;
   }
   return g;
 }
@@ -882,7 +892,7 @@ __global__ __launch_bounds__(kThreads, kRingPath ? SmallTile::kOccupancy : 1) vo
     int64_t P, int tiles_n) {
   using C = SmallTile;
   SHARQ_GEMM_LDS(C, kRingPath)
-  const GroupedTile g = grouped_tile<C, false>(seg, E, P, a_rows, tiles_n);
+  const GroupedTile g = grouped_tile<C, false>(seg, E, P, a_rows, op.a_rows_total, tiles_n);
   if (g.e < 0) return;  // uniform across the workgroup
   const int64_t n0 = (int64_t)g.col * C::BN;
   select_expert(op, g.e, w_codes_all, w_scales_all);
@@ -993,6 +1003,7 @@ __global__ __launch_bounds__(C::kThreads, C::kOccupancy) void linear_silu_prepar
   tr.m0 = (int64_t)tm * C::BM;
   tr.rows_valid = out.T - tr.m0 < C::BM ? out.T - tr.m0 : C::BM;
   tr.gather = nullptr;
+  tr.src_rows = out.T;
   const int64_t h0 = (int64_t)tn * 128;
   v16f acc[C::WM][C::WN];
   zero_acc<C>(acc);
@@ -1074,7 +1085,7 @@ __global__ __launch_bounds__(kThreads, SmallTile::kOccupancy) void linear_groupe
   using C = SmallTile;
   static_assert(C::kRing * C::kStage >= 128 * kHStride, "the h tile must fit in the ring's LDS");
   SHARQ_GEMM_LDS(C, true)
-  const GroupedTile g = grouped_tile<C, true>(seg, E, out.T, a_rows, tiles_n);
+  const GroupedTile g = grouped_tile<C, true>(seg, E, out.T, a_rows, op.a_rows_total, tiles_n);
   if (g.e < 0) return;
   const int64_t h0 = (int64_t)g.col * 128;
   select_expert(op, g.e, w_codes_all, w_scales_all);

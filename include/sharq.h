@@ -28,6 +28,18 @@
  * bytes (the quantisers write them; inputs from elsewhere must hold zeros).
  * One GEMM stage of a row tile is then one contiguous run of each operand.
  *
+ * This departs from the plain row-major contract (codes [R][K/2], scales
+ * [R][K/32]) that an MXFP4 interface would otherwise expose: every prepare
+ * output and every weight here is stage-major. The reason is measured GEMM
+ * time on MI355X: with row-major scales each 128-entry stage of a 128-row
+ * tile gathers 128 separate 4-byte scale runs, and with row-major codes 128
+ * separate 64-byte code runs; stage-major scales made the two-path GEMM
+ * 11-17% faster and stage-major codes another 5-9%. The canonical layout
+ * stays available at the boundary: sharq_pack_stage_major and
+ * sharq_unpack_stage_major convert in both directions without changing any
+ * byte, so a caller holding canonical tensors packs them once (weights) or
+ * unpacks prepare's output when it needs row-major codes.
+ *
  * Conventions for every entry point below:
  *  - Pointers are DEVICE pointers unless stated otherwise; the caller owns
  *    every buffer; the library allocates nothing and keeps no state, so calls
@@ -78,7 +90,9 @@ SHARQ_API int sharq_abi_version(void);
  * operator; Section 1: the residual is taken against the quantised backbone).
  *
  *  x        bf16 [T][ldx], the first K entries of each row are used.
- *  gamma    bf16 [K] RMSNorm weight absorbed as x' = x * gamma (fp32), or NULL.
+ *  gamma    bf16 [K] RMSNorm weight absorbed as x' = x * gamma (fp32), or NULL;
+ *           K entries are read, so it must hold at least K (the library cannot
+ *           check the length of a device buffer).
  *  n, m     N:M pattern: (2,4) or (8,16). Selection keeps, in each group of m
  *           consecutive K entries, the n largest |x'|; equal |x'| go to the
  *           lower index.
@@ -109,6 +123,7 @@ SHARQ_API int sharq_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx
  * power of two); mean, eps, sqrt and reciprocal are correctly rounded float64
  * operations. Two kernels run: the row scales, then the prepare.
  *  eps        > 0 and finite.
+ *  gamma      bf16 [K] or NULL, K entries read (as sharq_prepare).
  *  rms_scale  fp32 [T], written with r (required).
  *  other arguments as sharq_prepare. Requires K / 32 <= 4096
  *  (SHARQ_ENOTIMPL otherwise).
@@ -414,6 +429,7 @@ SHARQ_API int sharq_unpack_stage_major(const uint8_t* codes, const uint8_t* scal
  * scales). The residual is r = fp32(x' - fp32(e2m1 * e4m3 * tensor_scale)).
  *  bb_codes, res_codes    u8 [G][T][64]
  *  bb_scales, res_scales  u8 [G][T][8] (E4M3 bytes)
+ *  gamma                  bf16 [K] or NULL, K entries read (as sharq_prepare).
  *  other arguments and requirements as sharq_prepare.
  */
 SHARQ_API int sharq_prepare_nvfp4(const uint16_t* x, int64_t T, int64_t K, int64_t ldx,

@@ -161,3 +161,37 @@ def assert_bf16_close(h, want):
         i = tuple(np.argwhere(~ok)[0])
         raise AssertionError(f"{(~ok).sum()} bf16 values off by more than one ulp; first {i}: "
                              f"gpu {h[i]:#06x} want {want[i]:#06x}")
+
+
+def assert_h_close(h_bits, g_ref, g_bound, u_ref, u_bound):
+    """A fused gate|up kernel's h = bf16(silu(g) * u), computed on the GPU's own
+    fp32 g and u, against the oracle's float64 g and u (linear_ref and its
+    bound B for the gate and the up column).
+
+    The GPU's g and u lie within tau = 1e-4 B + 1e-6 of the oracle's (the Y
+    tolerance). |d silu / dg| <= 1.1 everywhere (its extremes are about 1.0998
+    and -0.0998), so silu(g) * u moves by at most
+        delta = 1.1 (|u| + tau_u) tau_g + (|silu(g)| + 1.1 tau_g) tau_u;
+    rounding to bf16 (and the fp32 arithmetic before it) adds at most one bf16
+    ulp of the result's magnitude, and fp32 intermediates may flush below
+    2^-126. Passes when |h - silu(g_ref) u_ref| <= delta + ulp + 2^-126."""
+    from synth import bf16_to_f32
+    h = bf16_to_f32(np.asarray(h_bits, dtype=np.uint16)).astype(np.float64)
+    g = np.asarray(g_ref, dtype=np.float64)
+    u = np.asarray(u_ref, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        silu = g / (1.0 + np.exp(-g))
+    f = silu * u
+    tg = TOL_REL * np.asarray(g_bound, dtype=np.float64) + TOL_ABS
+    tu = TOL_REL * np.asarray(u_bound, dtype=np.float64) + TOL_ABS
+    delta = 1.1 * (np.abs(u) + tu) * tg + (np.abs(silu) + 1.1 * tg) * tu
+    mag = np.maximum(np.abs(f) + delta, 2.0 ** -126)
+    ulp = np.ldexp(1.0, np.frexp(mag)[1] - 1 - 7)
+    tol = delta + ulp + 2.0 ** -126
+    err = np.abs(h - f)
+    bad = err > tol
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{bad.sum()} of {bad.size} h values outside tolerance; first {i}: gpu {h[i]} "
+                             f"oracle silu(g)*u {f[i]} (g {g[i]}, u {u[i]}) tol {tol[i]}")
+    return float((err / tol).max())

@@ -53,6 +53,14 @@ def test_output_buffers_are_checked(sq):
         sq.linear_nvfp4(pn, wn, out=torch.empty((T, O - 1), **f32))
     with pytest.raises(ValueError):
         sq.prepare_nvfp4(x, 0.01, out=sq.prepare_nvfp4(x[: T // 2], 0.01))
+    # gamma must hold exactly K entries (the kernels read K of them)
+    g_short = bf16_to_gpu(bf16_round(np.ones(K - 32, dtype=np.float32)))
+    with pytest.raises(ValueError):
+        sq.prepare(x, g_short)
+    with pytest.raises(ValueError):
+        sq.prepare(x, g_short, rms_eps=1e-5)
+    with pytest.raises(ValueError):
+        sq.prepare_nvfp4(x, 0.01, g_short)
     # well-formed buffers still work
     y = sq.linear(p, wq, out=torch.empty((T, O), **f32))
     torch.cuda.synchronize()

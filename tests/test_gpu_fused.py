@@ -5,17 +5,22 @@ other GPU tests check against the oracle.
 The fused kernel runs the same MFMA sequence per output element as the plain
 GEMM and the same SiLU and per-block prepare code, so h, codes, scales and
 masks must match the unfused chain bit for bit. On sampled rows the fused
-outputs are also checked against the oracle directly: prepare_ref of the
-fused h must reproduce the fused codes, scales and mask, and h must be the
-correctly rounded silu(g) * u of the GPU's GEMM output to one bf16 ulp.
+outputs are also checked against the oracle directly:
+  - h on sampled columns against silu(g) * u of the oracle's float64 gate and
+    up outputs (prepare_ref of x, quantize_weight_ref of the gate and up rows,
+    linear_ref), within the tolerance that the Y bound implies for h
+    (gpu_util.assert_h_close);
+  - prepare_ref of the fused h reproduces the fused codes, scales and mask;
+  - h is the correctly rounded silu(g) * u of the GPU's own GEMM output to
+    one bf16 ulp.
 """
 
 import numpy as np
 import pytest
 
-from oracle import prepare_ref, silu_mul_ref
+from oracle import linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref
 from synth import bf16_round, workload_llama8b_mlp
-from gpu_util import assert_bf16_close, assert_prepare_equal, bf16_to_gpu, to_np
+from gpu_util import assert_bf16_close, assert_h_close, assert_prepare_equal, bf16_to_gpu, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +73,20 @@ def _check_fused(sq, x_bits, gamma_bits, w_bits, n, m, rows_sample):
     rows = rows_sample
     assert_prepare_equal(hp, prepare_ref(h_np[rows], None, n, m), rows=rows)
     assert_bf16_close(h_np[rows], silu_mul_ref(to_np(y)[rows], I))
+    rng = np.random.default_rng(T + I)
+    cols = np.unique(np.concatenate([[0, I - 1], rng.choice(I, min(I, 48), replace=False)]))
+    check_h_against_oracle(h_np, x_bits, gamma_bits, w_bits[cols], w_bits[I + cols], rows, cols)
+
+
+def check_h_against_oracle(h_np, x_bits, gamma_bits, w_gate, w_up, rows, cols):
+    """The fused h on rows x cols against silu(g) * u of the oracle's float64
+    gate and up outputs; w_gate / w_up are the bf16 weight rows of those h
+    columns."""
+    o1 = prepare_ref(x_bits[rows], gamma_bits, 2, 4)
+    wc, ws = quantize_weight_ref(np.concatenate([w_gate, w_up]))
+    y_ref, bound = linear_ref(o1["bb_codes"], o1["bb_scales"], o1["res_codes"], o1["res_scales"], wc, ws)
+    nc = len(cols)
+    assert_h_close(h_np[np.ix_(rows, cols)], y_ref[:, :nc], bound[:, :nc], y_ref[:, nc:], bound[:, nc:])
 
 
 @pytest.mark.parametrize("T,I,K,n,m", [(300, 256, 512, 2, 4), (1, 128, 128, 2, 4), (130, 384, 1024, 8, 16),
@@ -116,7 +135,8 @@ def test_fused_llama70b_decode_gate_up(sq):
     g = torch.Generator(device="cuda").manual_seed(70)
     I, K = 28672, 8192
     assert _lib.call("sharq_linear_silu_prepare_workspace_bytes", 1, I, K) == 0, "no K split at this width"
-    w = sq.quantize_mxfp4((torch.randn(2 * I, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16))
+    w_bf16 = (torch.randn(2 * I, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    w = sq.quantize_mxfp4(w_bf16)
     rng = np.random.default_rng(70)
     x = bf16_round((rng.standard_normal((1, K)) * 2).astype(np.float32))
     p1 = sq.prepare(bf16_to_gpu(x), None, 2, 4)
@@ -131,3 +151,6 @@ def test_fused_llama70b_decode_gate_up(sq):
     h_np = to_np(h)
     assert_prepare_equal(hp, prepare_ref(h_np, None, 2, 4))
     assert_bf16_close(h_np, silu_mul_ref(to_np(y), I))
+    cols = np.unique(np.concatenate([[0, I - 1], rng.choice(I, 64, replace=False)]))
+    idx = torch.from_numpy(cols).cuda()
+    check_h_against_oracle(h_np, x, None, to_np(w_bf16[idx]), to_np(w_bf16[I + idx]), np.array([0]), cols)

@@ -220,3 +220,47 @@ def test_malformed_segments_and_indices_stay_in_bounds(sq):
     out = to_np(sq.moe_combine(yy[:P], torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()))
     ref, bnd = moe_combine_ref(to_np(yy[:P]), np.where(idx < P, idx, -1), w)
     assert np.all(np.abs(out - ref) <= 4 * 2.0 ** -24 * bnd + 1e-30)
+
+
+@pytest.mark.parametrize("K", [96, 256])
+def test_out_of_range_gather_rows_read_as_zero(sq, K):
+    """a_rows entries outside [0, T_src) (negative, just past the buffer, far
+    past it, past the 32-bit byte-offset range) read as all-zero activation
+    rows: their output rows are exactly zero, and every other row matches the
+    oracle. K = 96 takes the register-staged path, K = 256 the LDS ring."""
+    import torch
+    print(f"grouped out-of-range gather rows K={K}", flush=True)
+    rng = np.random.default_rng(43)
+    tokens, E, O = 150, 3, 256
+    x = bf16_round((rng.standard_normal((tokens, K)) * 2).astype(np.float32))
+    p = prepare_ref(x, None, 2, 4)
+    wc, ws = _experts(E, O, K, rng)
+    P = 180
+    rows = rng.integers(0, tokens, P).astype(np.int32)
+    bad = rng.choice(P, 40, replace=False)
+    rows[bad[:10]] = tokens
+    rows[bad[10:20]] = tokens + 1000
+    rows[bad[20:30]] = 1 << 30
+    rows[bad[30:]] = -7
+    seg = np.array([0, 50, 50, P], np.int32)  # expert 1 empty
+    y = to_np(sq.linear_grouped(oracle_prepared(p), w_to_gpu(wc, ws), i32_to_gpu(seg), i32_to_gpu(rows)))
+    torch.cuda.synchronize()
+    assert np.all(y[bad] == 0.0), "an out-of-range gathered row did not read as zeros"
+    # the oracle, with the bad rows pointed at an extra all-zero activation row
+    zero = prepare_ref(np.zeros((1, K), np.uint16), None, 2, 4)
+    ext = {f: np.concatenate([p[f], zero[f]]) for f in ("bb_codes", "bb_scales", "res_codes", "res_scales")}
+    ok_rows = np.where((rows >= 0) & (rows < tokens), rows, tokens).astype(np.int32)
+    y_ref, bound = linear_grouped_ref(ext["bb_codes"], ext["bb_scales"], ext["res_codes"], ext["res_scales"],
+                                      ok_rows, seg, wc, ws)
+    assert_y_close(y, y_ref, bound)
+    if K % 128 == 0:
+        # the grouped fused gate|up kernel (I = O / 2 = 128): the bad rows' h is silu(0) * 0 = 0, and their
+        # prepared rows are prepare_ref of zeros
+        hp, h = sq.linear_grouped_silu_prepare(oracle_prepared(p), w_to_gpu(wc, ws), i32_to_gpu(seg),
+                                               i32_to_gpu(rows), 2, 4, with_h=True)
+        torch.cuda.synchronize()
+        h_np = to_np(h)
+        assert np.all((h_np[bad] & 0x7FFF) == 0), "fused: an out-of-range gathered row gave non-zero h"
+        assert_prepare_equal(hp, prepare_ref(h_np[bad], None, 2, 4), rows=bad)
+        good = np.setdiff1d(np.arange(P), bad)
+        assert_bf16_close(h_np[good], silu_mul_ref(y[good], O // 2))

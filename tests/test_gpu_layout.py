@@ -67,3 +67,31 @@ def test_linear_on_a_packed_weight(sq):
     # and the library's own quantiser gives the same packed weight
     wq = sq.quantize_mxfp4(bf16_to_gpu(wb))
     assert np.array_equal(to_np(wq.codes), to_np(w.codes)) and np.array_equal(to_np(wq.scales), to_np(w.scales))
+
+
+@pytest.mark.parametrize("T,K,n,m,with_gamma", [(37, 352, 2, 4, False), (300, 1024, 8, 16, True),
+                                                  (2048, 4096, 2, 4, True), (64, 8192, 8, 16, False)])
+def test_prepare_output_in_canonical_layout(sq, T, K, n, m, with_gamma):
+    """The library's own prepare output, taken back to the canonical row-major
+    layout by sharq_unpack_stage_major on the GPU, equals prepare_ref's
+    canonical arrays byte for byte; the same for sharq_quantize_mxfp4 against
+    quantize_weight_ref."""
+    print(f"prepare -> unpack_stage_major T={T} K={K} {n}:{m} gamma={with_gamma}", flush=True)
+    rng = np.random.default_rng(T + K + n)
+    x = (rng.standard_normal((T, K)) * rng.lognormal(0, 0.5, (T, 1))).astype(np.float32)
+    x[:, rng.choice(K, max(1, K // 200), replace=False)] *= 50
+    x = bf16_round(x)
+    gamma = bf16_round(rng.uniform(0.5, 1.5, K).astype(np.float32)) if with_gamma else None
+    p = sq.prepare(bf16_to_gpu(x), None if gamma is None else bf16_to_gpu(gamma), n, m)
+    want = prepare_ref(x, gamma, n, m)
+    for path in ("bb", "res"):
+        c_rm, s_rm = sq.unpack_stage_major(getattr(p, f"{path}_codes"), getattr(p, f"{path}_scales"), K)
+        assert np.array_equal(to_np(c_rm), want[f"{path}_codes"]), f"{path} codes"
+        assert np.array_equal(to_np(s_rm), want[f"{path}_scales"]), f"{path} scales"
+    assert np.array_equal(to_np(p.mask), want["mask"])
+    O = 96
+    wb = bf16_round((rng.standard_normal((O, K)) * 0.02).astype(np.float32))
+    wq = sq.quantize_mxfp4(bf16_to_gpu(wb))
+    wc, ws = quantize_weight_ref(wb)
+    c_rm, s_rm = sq.unpack_stage_major(wq.codes, wq.scales, K)
+    assert np.array_equal(to_np(c_rm), wc) and np.array_equal(to_np(s_rm), ws)

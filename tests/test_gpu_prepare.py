@@ -154,7 +154,8 @@ def _rows_sample(T, count, seed):
 
 
 @pytest.mark.parametrize("name", ["linear_128x4096", "llama8b_x", "down_silu_8of16", "down_silu_2of4",
-                                  "qwen3_tokens", "llama70b_T64", "llama70b_T1"])
+                                  "qwen3_tokens", "llama70b_T64", "llama70b_T32", "llama70b_T8",
+                                  "llama70b_T1"])
 def test_prepare_workloads_full_size(sq, name):
     print(f"prepare workload {name}", flush=True)
     gamma = None

@@ -68,7 +68,7 @@ def test_split_k_workspace_shared_across_shapes(sq):
         seen[seed] = y
 
 
-@pytest.mark.parametrize("T", [1, 64])
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
 def test_llama70b_decode_shapes_full_size(sq, T):
     # the benchmark's decode GEMMs at full size, in the launch configuration it times (split K, 32- and
     # 64-row decode tiles): gate|up 2 x 28672 x 8192 and down 8192 x 28672, against the oracle on sampled

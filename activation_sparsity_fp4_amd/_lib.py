@@ -18,6 +18,8 @@ SHARQ_EALIGN = -2
 SHARQ_EUNSUPPORTED = -3
 SHARQ_EHIP = -4
 SHARQ_ENOTIMPL = -5
+SHARQ_ESCRATCH = -6
+SCRATCHFREE_MAX_BYTES = 32 << 20  # SHARQ_SCRATCHFREE_MAX_BYTES
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -40,6 +42,7 @@ SIGNATURES = {
     "sharq_linear": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "sharq_linear_workspace_bytes": (_I64, [_I64, _I64, _I64]),
     "sharq_linear_silu_prepare_workspace_bytes": (_I64, [_I64, _I64, _I64]),
+    "sharq_linear_scratchfree": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "sharq_linear_ws": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _I64, _P]),
     "sharq_linear_grouped": (_INT, [_P, _P, _P, _P, _I64, _P, _P, ctypes.c_int32, _P, _P, _I64, _I64, _I64, _P,
                                     _P]),

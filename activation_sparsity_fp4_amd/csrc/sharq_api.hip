@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 // Workgroups of one grouped launch: a one-dimensional grid of 256-thread
 // workgroups whose thread count must stay below 2^32.
 constexpr int64_t kMaxGroupedTiles = (int64_t)1 << 24;
@@ -81,6 +81,7 @@ const char* sharq_status_string(int status) {
     case SHARQ_EUNSUPPORTED: return "unsupported N:M pattern (supported: 2:4, 8:16)";
     case SHARQ_EHIP: return "HIP launch failed";
     case SHARQ_ENOTIMPL: return "not implemented";
+    case SHARQ_ESCRATCH: return "the call needs more scratch memory than the static maximum";
     default: return "unknown status";
   }
 }
@@ -194,6 +195,21 @@ int64_t sharq_linear_workspace_bytes(int64_t T, int64_t O, int64_t K) {
   if (T < 0 || O < 0 || K <= 0 || K % 32 != 0) return 0;
   if (T >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return 0;
   return sharq::linear_workspace_bytes(T, O, K);
+}
+
+int sharq_linear_scratchfree(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                             const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales, int64_t T,
+                             int64_t O, int64_t K, float* y, int64_t ldy, hipStream_t stream) {
+  if (T < 0 || O < 0 || K <= 0 || K % 32 != 0 || ldy < O) return SHARQ_EINVAL;
+  if (T >= ((int64_t)1 << 31) || O >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return SHARQ_EINVAL;
+  if (T == 0 || O == 0) return SHARQ_OK;
+  if (!bb_codes || !bb_scales || !res_codes || !res_scales || !w_codes || !w_scales || !y) return SHARQ_EINVAL;
+  if (!aligned16(bb_codes) || !aligned16(bb_scales) || !aligned16(res_codes) || !aligned16(res_scales) ||
+      !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y))
+    return SHARQ_EALIGN;
+  if (!sharq::linear_scratchfree_fits(T, O, K)) return SHARQ_ESCRATCH;
+  return hip_status(sharq::launch_linear_scratchfree(bb_codes, bb_scales, res_codes, res_scales, w_codes, w_scales,
+                                                     T, O, K, y, ldy, stream));
 }
 
 int sharq_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,

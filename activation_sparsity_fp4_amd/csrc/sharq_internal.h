@@ -27,6 +27,13 @@ hipError_t launch_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales, c
                             int64_t O, int64_t K, float* y, int64_t ldy, void* workspace, int64_t workspace_bytes,
                             hipStream_t stream);
 
+// The scratch-free split-K GEMM (scratchfree.hip): whether the split plan's
+// partials fit its static array, and the launch.
+bool linear_scratchfree_fits(int64_t T, int64_t O, int64_t K);
+hipError_t launch_linear_scratchfree(const uint8_t* bb_codes, const uint8_t* bb_scales, const uint8_t* res_codes,
+                                     const uint8_t* res_scales, const uint8_t* w_codes, const uint8_t* w_scales,
+                                     int64_t T, int64_t O, int64_t K, float* y, int64_t ldy, hipStream_t stream);
+
 hipError_t launch_linear_grouped(const uint8_t* bb_codes, const uint8_t* bb_scales,
                                  const uint8_t* res_codes, const uint8_t* res_scales,
                                  const int32_t* a_rows, const int32_t* seg_offsets, int32_t E,

@@ -75,7 +75,8 @@ typedef enum {
   SHARQ_EALIGN = -2,       /* pointer not 16-byte aligned, or ldx % 8 != 0 */
   SHARQ_EUNSUPPORTED = -3, /* (n, m) not in {(2,4), (8,16)} */
   SHARQ_EHIP = -4,         /* the HIP launch itself failed */
-  SHARQ_ENOTIMPL = -5      /* a shape class this library does not handle */
+  SHARQ_ENOTIMPL = -5,     /* a shape class this library does not handle */
+  SHARQ_ESCRATCH = -6      /* needs more scratch than SHARQ_SCRATCHFREE_MAX_BYTES */
 } sharq_status;
 
 /* Host. Static string describing a status code; never NULL. */
@@ -191,6 +192,33 @@ SHARQ_API int sharq_linear_ws(const uint8_t* bb_codes, const uint8_t* bb_scales,
                     const uint8_t* w_codes, const uint8_t* w_scales,
                     int64_t T, int64_t O, int64_t K, float* y, int64_t ldy,
                     void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sharq_linear_scratchfree -- sharq_linear_ws without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments and result as sharq_linear, bit-identical to
+ * sharq_linear_ws with a large enough workspace (the same split plan and
+ * kernels).
+ *
+ * The split-K partials live in a static device array of
+ * SHARQ_SCRATCHFREE_MAX_BYTES bytes that every GPU the library runs on holds
+ * from load until the process ends. Every call on one GPU shares that GPU's
+ * array: calls that may overlap in time on one GPU (several streams or host
+ * threads) race and give undefined results; serialise them. The array's
+ * contents need no initialisation (each call writes every partial it reads).
+ *
+ * Errors: as sharq_linear; SHARQ_ESCRATCH, before any HIP call, when the
+ * split plan needs more than SHARQ_SCRATCHFREE_MAX_BYTES
+ * (sharq_linear_workspace_bytes(T, O, K) tells how much it needs). The first
+ * call on a device looks up the array's device address (no allocation).
+ */
+#define SHARQ_SCRATCHFREE_MAX_BYTES ((int64_t)32 << 20)
+SHARQ_API int sharq_linear_scratchfree(const uint8_t* bb_codes, const uint8_t* bb_scales,
+                             const uint8_t* res_codes, const uint8_t* res_scales,
+                             const uint8_t* w_codes, const uint8_t* w_scales,
+                             int64_t T, int64_t O, int64_t K, float* y, int64_t ldy,
+                             hipStream_t stream);
 
 /*
  * sharq_linear_grouped -- sharq_linear per expert segment, for mixture-of-

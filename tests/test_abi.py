@@ -41,8 +41,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert _lib.call("sharq_abi_version") == 9
-    for s in (0, -1, -2, -3, -4, -5):
+    assert _lib.call("sharq_abi_version") == 10
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert _lib.status_string(s)
     assert _lib.status_string(-99) == "unknown status"
 
@@ -92,6 +92,30 @@ def test_linear_validation():
     assert lin(T=-3) == _lib.SHARQ_EINVAL
     assert lin(ws=F + 1) == _lib.SHARQ_EALIGN
     assert lin(y=G + 4) == _lib.SHARQ_EALIGN
+
+
+def lin_sf(T=4, O=8, K=64, y=G, ldy=8, **kw):
+    args = dict(bc=A, bs=B, rc=C, rs=D, wc=E_, ws=F)
+    args.update(kw)
+    return _lib.call("sharq_linear_scratchfree", args["bc"], args["bs"], args["rc"], args["rs"], args["wc"],
+                     args["ws"], T, O, K, y, ldy, 0)
+
+
+def test_linear_scratchfree_validation():
+    """The scratch-free GEMM checks its arguments as sharq_linear does, and
+    refuses, before any HIP call, a shape whose split-K partials exceed the
+    static scratch array."""
+    assert lin_sf(T=0) == _lib.SHARQ_OK
+    assert lin_sf(y=0) == _lib.SHARQ_EINVAL
+    assert lin_sf(K=48) == _lib.SHARQ_EINVAL
+    assert lin_sf(ldy=4) == _lib.SHARQ_EINVAL
+    assert lin_sf(ws=F + 1) == _lib.SHARQ_EALIGN
+    T, O, K = 320, 8192, 28672
+    assert _lib.call("sharq_linear_workspace_bytes", T, O, K) > _lib.SCRATCHFREE_MAX_BYTES
+    assert lin_sf(T=T, O=O, K=K, ldy=O) == _lib.SHARQ_ESCRATCH
+    assert _lib.status_string(_lib.SHARQ_ESCRATCH) != "unknown status"
+    header = open(HEADER).read()
+    assert re.search(r"#define SHARQ_SCRATCHFREE_MAX_BYTES \(\(int64_t\)32 << 20\)", header)
 
 
 def grp(P=16, O=8, K=64, E=2, a_rows=A, seg=B, T_src=16, **kw):

@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the SharQ linear hot path on one MI355X.
 
-Default workload: a Llama-3.1-8B-shaped MLP block at 2048-token prefill, 2:4,
+Headline workload: a Llama-3.1-8B-shaped MLP block at 2048-token prefill, 2:4,
 MXFP4, the RMSNorm (per-row 1/rms and gamma) absorbed in the first prepare:
     prepare(rmsnorm(x)) -> fused [two-path GEMM gate|up [28672 x 4096] ->
     silu(gate) * up -> prepare(h)] -> two-path GEMM down [4096 x 14336]
@@ -9,9 +9,22 @@ One step = one pass of that chain over 2048 tokens. Inputs are seeded synthetic
 data resident in HBM before the timed region; weights are quantised once on
 the GPU (not timed).
 
-Prints ONE JSON line with tokens/s, the per-stage breakdown (HIP events on the
-launch stream), the roofline of the dominant kernel and the CPU oracle timed on
-a bounded sample of the same workload. Other workloads: --workload NAME.
+Timed region: K replays of the step captured once as a HIP graph (kernel
+nodes only; inside it the kernels run back to back), HIP events recorded on
+the launch stream before and after them; `value` is tokens over the
+wall-clock time of the K steps. Before it, W warm-up steps and half a second
+of untimed replays: the GPU boosts its clocks for the first milliseconds of a
+load and then settles to its sustained (power-limited) clock, which is what
+the timed region measures. Stage (kernel) times come from a graph of back-to-back
+launches of each stage alone, HIP events around its replays. The same step
+launched eagerly (HIP events between the stages) is reported beside it.
+
+Prints ONE JSON line: tokens/s, the per-stage breakdown, the roofline of the
+dominant kernel, a `configs` object with the other workloads (single linear
+128x4096, down_proj 2048x14336 8:16 and 2:4, Llama-3.1-70B decode at T = 1, 8,
+32, 64 with three rotated weight copies, Qwen3-30B-A3B MoE layer) and the CPU
+oracle timed in a child process on a bounded sample of the headline workload.
+Other workloads as the headline: --workload NAME.
 """
 
 from __future__ import annotations
@@ -19,6 +32,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -35,6 +49,12 @@ F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 MFMA (the NVFP4 GEMM widens i
 WORKLOADS = ["llama8b_mlp", "linear_128x4096", "down_8of16", "down_2of4", "llama70b_decode_T1",
              "llama70b_decode_T8", "llama70b_decode_T32", "llama70b_decode_T64", "qwen3_moe", "compact_2of4",
              "compact_8of16", "nvfp4_down_8of16", "nvfp4_down_2of4"]
+
+# the other configurations reported in the `configs` object of the default run
+CONFIG_SET = [("c1", "linear_128x4096"), ("c3_8of16", "down_8of16"), ("c3_2of4", "down_2of4"),
+              ("c4_T1", "llama70b_decode_T1"), ("c4_T8", "llama70b_decode_T8"),
+              ("c4_T32", "llama70b_decode_T32"), ("c4_T64", "llama70b_decode_T64"), ("c5", "qwen3_moe")]
+DECODE_COPIES = 3  # resident weight copies the decode steps rotate through (together 1.1 GB > 256 MB MALL)
 
 
 def prepare_bytes(T, K, gamma=False):
@@ -63,10 +83,6 @@ def fused_bytes(T, I, H):
     return 2 * T * H * 17 / 32 + 2 * I * H * 17 / 32 + T * I * (0.5 + 0.5 + 2 / 32 + 1 / 8)
 
 
-def _to_gpu_bf16(torch, u16):
-    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
-
-
 def nv_prepare_bytes(T, K):
     """NVFP4 prepare: read bf16 x, write two code arrays (0.5/elem each), two E4M3
     scale arrays (1/16 each) and the mask (1/8)."""
@@ -78,17 +94,52 @@ def nv_gemm_bytes(T, O, K):
     return 2 * T * K * 9 / 16 + O * K * 9 / 16 + 4 * T * O
 
 
+def _to_gpu_bf16(torch, u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _gpu_normal_bf16(torch, rows, cols, seed, sigma=0.02):
+    """bf16 [rows x cols] with N(0, sigma) entries drawn on the GPU from a seeded generator."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return (torch.randn(rows, cols, device="cuda", generator=g) * sigma).to(torch.bfloat16)
+
+
 class Stage:
+    """One kernel launch of a step. fn(c) launches it against weight copy c."""
+
     def __init__(self, name, fn, kind, bytes_=0.0, flops_alg=0.0, flops_exec=0.0, peak=FP4_PEAK_TFLOPS):
         self.name, self.fn, self.kind = name, fn, kind
         self.bytes, self.flops_alg, self.flops_exec = bytes_, flops_alg, flops_exec
         self.peak = peak  # TFLOP/s of the matrix unit the stage runs on
 
 
+class Workload:
+    def __init__(self, stages, tokens, cfg, copies=1, oracle=None):
+        self.stages, self.tokens, self.cfg, self.copies, self.oracle = stages, tokens, cfg, copies, oracle
+
+
+_DECODE_WEIGHTS = {}
+
+
+def decode_weights(torch, sq, H, I, copies):
+    """The Llama-3.1-70B gate|up [2I x H] and down [H x I] weights, `copies`
+    independent draws (seeds 7000 + 2c, 7001 + 2c), quantised on the GPU;
+    shared by the four decode workloads."""
+    key = (H, I, copies)
+    if key not in _DECODE_WEIGHTS:
+        ws = []
+        for c in range(copies):
+            w_gu = sq.quantize_mxfp4(_gpu_normal_bf16(torch, 2 * I, H, 7000 + 2 * c))
+            w_dn = sq.quantize_mxfp4(_gpu_normal_bf16(torch, H, I, 7001 + 2 * c))
+            ws.append((w_gu, w_dn))
+            torch.cuda.synchronize()
+        _DECODE_WEIGHTS[key] = ws
+    return _DECODE_WEIGHTS[key]
+
+
 def build_workload(name, torch, sq, unfused=False):
-    """Returns (stages, tokens_per_step, config dict, oracle sample fn)."""
-    from synth import (workload_down_silu, workload_linear, workload_llama70b_decode, workload_llama8b_mlp,
-                       workload_qwen3_moe)
+    from synth import (array_digest, workload_down_silu, workload_linear, workload_llama70b_decode,
+                       workload_llama8b_mlp, workload_qwen3_moe)
     if name == "llama8b_mlp":
         wl = workload_llama8b_mlp()
         T, H, I = wl["x"].shape[0], wl["hidden"], wl["inter"]
@@ -96,8 +147,7 @@ def build_workload(name, torch, sq, unfused=False):
         w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"]))
         w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"]))
         eps = 1e-5  # Llama-3.1 RMSNorm epsilon
-        buf = {}
-        buf["p1"] = sq.prepare(x, g, 2, 4, rms_eps=eps)
+        buf = {"p1": sq.prepare(x, g, 2, 4, rms_eps=eps)}
         fa1, fe1 = gemm_flops(T, 2 * I, H)
         fa2, fe2 = gemm_flops(T, H, I)
         if unfused:
@@ -105,44 +155,31 @@ def build_workload(name, torch, sq, unfused=False):
             buf["h"] = sq.silu_mul(buf["gu"])
             buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
             middle = [
-                Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "mfma",
+                Stage("gemm_gate_up", lambda c=0: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "mfma",
                       gemm_bytes(T, 2 * I, H), fa1, fe1),
-                Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
-                Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
+                Stage("silu_mul", lambda c=0: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
+                Stage("prepare_h", lambda c=0: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
                       prepare_bytes(T, I)),
             ]
         else:
             buf["p2"], _ = sq.linear_silu_prepare(buf["p1"], w_gu, 2, 4)
             middle = [
                 Stage("gemm_gate_up_silu_prepare",
-                      lambda: sq.linear_silu_prepare_into(buf["p1"], w_gu, buf["p2"], 2, 4), "mfma",
+                      lambda c=0: sq.linear_silu_prepare_into(buf["p1"], w_gu, buf["p2"], 2, 4), "mfma",
                       fused_bytes(T, I, H), fa1, fe1),
             ]
         buf["y"] = sq.linear(buf["p2"], w_dn)
-        stages = [Stage("prepare_x_rmsnorm", lambda: sq.prepare(x, g, 2, 4, out=buf["p1"], rms_eps=eps), "hbm",
+        stages = [Stage("prepare_x_rmsnorm", lambda c=0: sq.prepare(x, g, 2, 4, out=buf["p1"], rms_eps=eps), "hbm",
                         prepare_bytes(T, H, True) + 4 * T)] + middle + [
-            Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "mfma", gemm_bytes(T, H, I), fa2, fe2),
+            Stage("gemm_down", lambda c=0: sq.linear(buf["p2"], w_dn, out=buf["y"]), "mfma", gemm_bytes(T, H, I),
+                  fa2, fe2),
         ]
-        from synth import array_digest
         cfg = {"workload": "Llama-3.1-8B MLP block, 2048-token prefill, 2:4, MXFP4, RMSNorm (1/rms and gamma) "
                            "absorbed in the first prepare",
                "tokens": T, "hidden": H, "intermediate": I, "nm": "2:4", "rms_eps": eps, "seed": 1002,
                "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)",
                "input_sha256_16": {k: array_digest(wl[k]) for k in ("x", "gamma", "w_gu", "w_down")}}
-
-        def oracle_sample(rows):
-            from oracle import linear_ref, prepare_ref, quantize_weight_ref, silu_mul_ref
-            xs = wl["x"][:rows]
-            t0 = time.perf_counter()
-            p1 = prepare_ref(xs, wl["gamma"], 2, 4, rms_eps=1e-5)
-            wc, ws = quantize_weight_ref(wl["w_gu"])
-            gu, _ = linear_ref(p1["bb_codes"], p1["bb_scales"], p1["res_codes"], p1["res_scales"], wc, ws)
-            h = silu_mul_ref(gu.astype(np.float32), I)
-            p2 = prepare_ref(h, None, 2, 4)
-            wc, ws = quantize_weight_ref(wl["w_down"])
-            linear_ref(p2["bb_codes"], p2["bb_scales"], p2["res_codes"], p2["res_scales"], wc, ws)
-            return time.perf_counter() - t0
-        return stages, T, cfg, oracle_sample
+        return Workload(stages, T, cfg, oracle="llama8b_mlp")
 
     if name == "linear_128x4096" or name.startswith("down_"):
         if name == "linear_128x4096":
@@ -161,18 +198,11 @@ def build_workload(name, torch, sq, unfused=False):
         buf = {"p": sq.prepare(x, None, n, m)}
         buf["y"] = sq.linear(buf["p"], wq)
         fa, fe = gemm_flops(T, O, K, n, m)
-        stages = [Stage("prepare", lambda: sq.prepare(x, None, n, m, out=buf["p"]), "hbm", prepare_bytes(T, K)),
-                  Stage("gemm", lambda: sq.linear(buf["p"], wq, out=buf["y"]), "mfma", gemm_bytes(T, O, K), fa, fe)]
+        kind = "mfma" if T >= 1024 else "hbm"
+        stages = [Stage("prepare", lambda c=0: sq.prepare(x, None, n, m, out=buf["p"]), "hbm", prepare_bytes(T, K)),
+                  Stage("gemm", lambda c=0: sq.linear(buf["p"], wq, out=buf["y"]), kind, gemm_bytes(T, O, K), fa, fe)]
         cfg = {"workload": label, "tokens": T, "in_features": K, "out_features": O, "nm": f"{n}:{m}"}
-
-        def oracle_sample(rows):
-            from oracle import linear_ref, prepare_ref, quantize_weight_ref
-            t0 = time.perf_counter()
-            p = prepare_ref(xb[:rows], None, n, m)
-            wc, ws = quantize_weight_ref(wb)
-            linear_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], wc, ws)
-            return time.perf_counter() - t0
-        return stages, T, cfg, oracle_sample
+        return Workload(stages, T, cfg)
 
     if name.startswith("nvfp4_down_"):
         # the down projection with NVFP4 operands (16-entry blocks, E4M3 block scales, fp32 tensor scales)
@@ -190,26 +220,18 @@ def build_workload(name, torch, sq, unfused=False):
         buf = {"p": sq.prepare_nvfp4(x, s_a, None, n, m)}
         buf["y"] = sq.linear_nvfp4(buf["p"], wq)
         fa, fe = gemm_flops(T, O, K, n, m)
-        stages = [Stage("prepare_nvfp4", lambda: sq.prepare_nvfp4(x, s_a, None, n, m, out=buf["p"]), "hbm",
+        stages = [Stage("prepare_nvfp4", lambda c=0: sq.prepare_nvfp4(x, s_a, None, n, m, out=buf["p"]), "hbm",
                         nv_prepare_bytes(T, K)),
-                  Stage("gemm_nvfp4", lambda: sq.linear_nvfp4(buf["p"], wq, out=buf["y"]), "mfma",
+                  Stage("gemm_nvfp4", lambda c=0: sq.linear_nvfp4(buf["p"], wq, out=buf["y"]), "mfma",
                         nv_gemm_bytes(T, O, K), fa, fe, F16_PEAK_TFLOPS)]
         cfg = {"workload": f"down_proj 2048x14336 -> 4096, {n}:{m}, NVFP4 (GEMM on fp16 MFMA), SiLU-gated input",
                "tokens": T, "in_features": K, "out_features": O, "nm": f"{n}:{m}", "format": "nvfp4",
                "tensor_scales": {"activation": s_a, "weight": s_w}}
-
-        def oracle_sample(rows):
-            from oracle import linear_nvfp4_ref, prepare_nvfp4_ref, quantize_weight_nvfp4_ref
-            t0 = time.perf_counter()
-            p = prepare_nvfp4_ref(xb[:rows], None, n, m, s_a)
-            wc, ws = quantize_weight_nvfp4_ref(wb, s_w)
-            linear_nvfp4_ref(p["bb_codes"], p["bb_scales"], p["res_codes"], p["res_scales"], s_a, wc, ws, s_w)
-            return time.perf_counter() - t0
-        return stages, T, cfg, oracle_sample
+        return Workload(stages, T, cfg)
 
     if name.startswith("compact_"):
         # compressed backbone of the down projection's input: prepare, compress, expand
-        wl = workload_down_silu()
+        wl = workload_down_silu(with_weights=False)
         xb = wl["x"]
         n, m = (8, 16) if name == "compact_8of16" else (2, 4)
         T, K = xb.shape
@@ -220,62 +242,64 @@ def build_workload(name, torch, sq, unfused=False):
         meta = buf["c"].meta.shape[1]
         dense = T * K * (0.5 + 1 / 8)            # dense backbone codes + mask
         packed = T * (K / 4 + meta)              # kept codes + rank fields
-        stages = [Stage("prepare", lambda: sq.prepare(x, None, n, m, out=buf["p"]), "hbm", prepare_bytes(T, K)),
-                  Stage("compress_backbone", lambda: sq.compress_backbone(buf["p"], n, m, out=buf["c"]), "hbm",
+        stages = [Stage("prepare", lambda c=0: sq.prepare(x, None, n, m, out=buf["p"]), "hbm", prepare_bytes(T, K)),
+                  Stage("compress_backbone", lambda c=0: sq.compress_backbone(buf["p"], n, m, out=buf["c"]), "hbm",
                         dense + packed),
-                  Stage("expand_backbone", lambda: sq.expand_backbone(buf["c"], buf["bb"], buf["mask"]), "hbm",
+                  Stage("expand_backbone", lambda c=0: sq.expand_backbone(buf["c"], buf["bb"], buf["mask"]), "hbm",
                         dense + packed)]
         cfg = {"workload": f"compressed sparse backbone of the down_proj input 2048x14336, {n}:{m}", "tokens": T,
                "in_features": K, "nm": f"{n}:{m}",
                "backbone_bytes_per_element": {"dense_codes_and_mask": 0.625, "compressed": round(packed / (T * K), 4)}}
-        return stages, T, cfg, None
+        return Workload(stages, T, cfg)
 
     if name.startswith("llama70b_decode_T"):
         T = int(name.split("_T")[1])
-        wl = workload_llama70b_decode(T)
+        wl = workload_llama70b_decode(T, with_weights=False)
         H, I = wl["hidden"], wl["inter"]
         x = _to_gpu_bf16(torch, wl["x"])
-        w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"]))
-        w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"]))
+        ws = decode_weights(torch, sq, H, I, DECODE_COPIES)
         buf = {"p1": sq.prepare(x, None, 2, 4)}
         fa1, fe1 = gemm_flops(T, 2 * I, H)
         fa2, fe2 = gemm_flops(T, H, I)
         if unfused:
-            buf["gu"] = sq.linear(buf["p1"], w_gu)
+            buf["gu"] = sq.linear(buf["p1"], ws[0][0])
             buf["h"] = sq.silu_mul(buf["gu"])
             buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
             middle = [
-                Stage("gemm_gate_up", lambda: sq.linear(buf["p1"], w_gu, out=buf["gu"]), "hbm",
+                Stage("gemm_gate_up", lambda c=0: sq.linear(buf["p1"], ws[c][0], out=buf["gu"]), "hbm",
                       gemm_bytes(T, 2 * I, H), fa1, fe1),
-                Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
-                Stage("prepare_h", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
+                Stage("silu_mul", lambda c=0: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(T, I)),
+                Stage("prepare_h", lambda c=0: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
                       prepare_bytes(T, I)),
             ]
         else:
-            buf["p2"], _ = sq.linear_silu_prepare(buf["p1"], w_gu, 2, 4)
+            buf["p2"], _ = sq.linear_silu_prepare(buf["p1"], ws[0][0], 2, 4)
             middle = [
                 Stage("gemm_gate_up_silu_prepare",
-                      lambda: sq.linear_silu_prepare_into(buf["p1"], w_gu, buf["p2"], 2, 4), "hbm",
+                      lambda c=0: sq.linear_silu_prepare_into(buf["p1"], ws[c][0], buf["p2"], 2, 4), "hbm",
                       fused_bytes(T, I, H), fa1, fe1),
             ]
-        buf["y"] = sq.linear(buf["p2"], w_dn)
-        stages = [Stage("prepare_x", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(T, H))
-                  ] + middle + [
-            Stage("gemm_down", lambda: sq.linear(buf["p2"], w_dn, out=buf["y"]), "hbm", gemm_bytes(T, H, I), fa2, fe2),
+        buf["y"] = sq.linear(buf["p2"], ws[0][1])
+        stages = [Stage("prepare_x", lambda c=0: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm",
+                        prepare_bytes(T, H))] + middle + [
+            Stage("gemm_down", lambda c=0: sq.linear(buf["p2"], ws[c][1], out=buf["y"]), "hbm", gemm_bytes(T, H, I),
+                  fa2, fe2),
         ]
         cfg = {"workload": f"Llama-3.1-70B MLP decode, {T} tokens, 2:4, MXFP4", "tokens": T, "hidden": H,
                "intermediate": I, "nm": "2:4",
-               "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)"}
-        return stages, T, cfg, None
+               "gate_up": "unfused (linear, silu_mul, prepare)" if unfused else "fused (linear_silu_prepare)",
+               "weight_copies": DECODE_COPIES,
+               "weights": "N(0, 0.02) drawn on the GPU (torch generator seeds 7000 + 2c, 7001 + 2c), MXFP4"}
+        return Workload(stages, T, cfg, copies=DECODE_COPIES)
 
     if name == "qwen3_moe":
-        wl = workload_qwen3_moe()
+        wl = workload_qwen3_moe(with_weights=False)
         E, I, H = wl["experts"], wl["inter"], wl["hidden"]
         P = len(wl["a_rows"])
         tokens = wl["x"].shape[0]
         x = _to_gpu_bf16(torch, wl["x"])
-        w_gu = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_gu"].reshape(E * 2 * I, H)).view(E, 2 * I, H))
-        w_dn = sq.quantize_mxfp4(_to_gpu_bf16(torch, wl["w_down"].reshape(E * H, I)).view(E, H, I))
+        w_gu = sq.quantize_mxfp4(_gpu_normal_bf16(torch, E * 2 * I, H, 5005).view(E, 2 * I, H))
+        w_dn = sq.quantize_mxfp4(_gpu_normal_bf16(torch, E * H, I, 5006).view(E, H, I))
         seg = torch.from_numpy(wl["seg_offsets"]).cuda()
         rows = torch.from_numpy(wl["a_rows"]).cuda()
         buf = {"p1": sq.prepare(x, None, 2, 4)}
@@ -287,18 +311,18 @@ def build_workload(name, torch, sq, unfused=False):
             buf["h"] = sq.silu_mul(buf["gu"])
             buf["p2"] = sq.prepare(buf["h"], None, 2, 4)
             middle = [
-                Stage("grouped_gate_up", lambda: sq.linear_grouped(buf["p1"], w_gu, seg, rows, out=buf["gu"]), "hbm",
-                      gu_in_bytes + 4 * P * 2 * I, fa1, fe1),
-                Stage("silu_mul", lambda: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(P, I)),
-                Stage("prepare_pairs", lambda: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
+                Stage("grouped_gate_up", lambda c=0: sq.linear_grouped(buf["p1"], w_gu, seg, rows, out=buf["gu"]),
+                      "hbm", gu_in_bytes + 4 * P * 2 * I, fa1, fe1),
+                Stage("silu_mul", lambda c=0: sq.silu_mul(buf["gu"], out=buf["h"]), "hbm", silu_bytes(P, I)),
+                Stage("prepare_pairs", lambda c=0: sq.prepare(buf["h"], None, 2, 4, out=buf["p2"]), "hbm",
                       prepare_bytes(P, I)),
             ]
         else:
             buf["p2"], _ = sq.linear_grouped_silu_prepare(buf["p1"], w_gu, seg, rows, 2, 4)
             middle = [
                 Stage("grouped_gate_up_silu_prepare",
-                      lambda: sq.linear_grouped_silu_prepare(buf["p1"], w_gu, seg, rows, 2, 4, out=buf["p2"]), "hbm",
-                      gu_in_bytes + prepare_bytes(P, I) - 2 * P * I, fa1, fe1),
+                      lambda c=0: sq.linear_grouped_silu_prepare(buf["p1"], w_gu, seg, rows, 2, 4, out=buf["p2"]),
+                      "hbm", gu_in_bytes + prepare_bytes(P, I) - 2 * P * I, fa1, fe1),
             ]
         buf["y"] = sq.linear_grouped(buf["p2"], w_dn, seg, None)
         from synth import moe_combine_index
@@ -307,22 +331,154 @@ def build_workload(name, torch, sq, unfused=False):
         cidx, cw = torch.from_numpy(cidx).cuda(), torch.from_numpy(cw).cuda()
         buf["out"] = sq.moe_combine(buf["y"], cidx, cw, bf16=True)
         stages = [
-            Stage("prepare_tokens", lambda: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm", prepare_bytes(tokens, H))
+            Stage("prepare_tokens", lambda c=0: sq.prepare(x, None, 2, 4, out=buf["p1"]), "hbm",
+                  prepare_bytes(tokens, H))
         ] + middle + [
-            Stage("grouped_down", lambda: sq.linear_grouped(buf["p2"], w_dn, seg, None, out=buf["y"]), "hbm",
+            Stage("grouped_down", lambda c=0: sq.linear_grouped(buf["p2"], w_dn, seg, None, out=buf["y"]), "hbm",
                   2 * P * I * 17 / 32 + E * H * I * 17 / 32 + 4 * P * H, fa2, fe2),
-            Stage("moe_combine", lambda: sq.moe_combine(buf["y"], cidx, cw, out=buf["out"], bf16=True), "hbm",
+            Stage("moe_combine", lambda c=0: sq.moe_combine(buf["y"], cidx, cw, out=buf["out"], bf16=True), "hbm",
                   4 * P * H + 2 * tokens * H + 8 * P),
         ]
         cfg = {"workload": "Qwen3-30B-A3B MoE expert layer, 4096 tokens, top-8 of 128, 2:4, MXFP4, weighted "
                            "combine to bf16 tokens",
                "tokens": tokens, "pairs": P, "experts": E, "hidden": H, "intermediate": I, "nm": "2:4",
                "gate_up": "unfused (linear_grouped, silu_mul, prepare)" if unfused
-               else "fused (linear_grouped_silu_prepare)"}
-        return stages, tokens, cfg, None
+               else "fused (linear_grouped_silu_prepare)",
+               "weights": "N(0, 0.02) drawn on the GPU (torch generator seeds 5005, 5006), MXFP4"}
+        return Workload(stages, tokens, cfg)
 
     raise SystemExit(f"unknown workload {name}; choose from {WORKLOADS}")
 
+
+# ---------------------------------------------------------------------------
+# Timing
+# ---------------------------------------------------------------------------
+
+def capture_step_graphs(torch, wl):
+    """One HIP graph per weight copy holding the whole step, captured after
+    warm-up. The library enqueues kernel launches only, so the graphs hold
+    kernel nodes only; inside a graph the kernels run back to back."""
+    graphs = []
+    for c in range(wl.copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in wl.stages:
+                s.fn(c)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_step_graphs(torch, graphs, steps):
+    """The timed region: K whole-step graph replays back to back (weight copies
+    rotated), one HIP event recorded on the launch stream before the first and
+    one after the last (an event between replays would itself add tens of us to
+    each step). Returns (ms per step from the wall clock, ms per step from the
+    two events)."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record()
+    for k in range(steps):
+        graphs[k % len(graphs)].replay()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return 1e3 * wall / steps, a.elapsed_time(b) / steps
+
+
+def settle(torch, graphs, seconds):
+    """Untimed replays of the step for `seconds`: the GPU's power management
+    raises clocks above their sustained level for the first milliseconds of a
+    load and throttles after that, so the timed region starts only once the
+    clocks have reached the sustained state."""
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            graphs[k % len(graphs)].replay()
+            k += 1
+        torch.cuda.synchronize()
+
+
+def time_stages_back_to_back(torch, wl, launches=10, reps=5):
+    """Per-stage kernel time as it runs inside a step graph: for each stage a
+    graph of `launches` back-to-back launches of that stage alone (weight copies
+    rotated launch by launch), replayed `reps` times with HIP events around each
+    replay; returns the median per-launch ms of each stage."""
+    out = []
+    for s in wl.stages:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(launches):
+                s.fn(r % wl.copies)
+        g.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for r in range(reps):
+            g.replay()
+            ev[r + 1].record()
+        torch.cuda.synchronize()
+        out.append(float(np.median([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)])) / launches)
+        del g
+    return out
+
+
+def time_eager(torch, wl, steps):
+    """K eager steps with events between the stages: (ms per step, [median ms per stage])."""
+    n = len(wl.stages)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        c = k % wl.copies
+        ev[k][0].record()
+        for i, s in enumerate(wl.stages):
+            s.fn(c)
+            ev[k][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [float(np.median([ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)])) for i in range(n)]
+    return 1e3 * wall / steps, stage_ms
+
+
+def warm(torch, wl, steps):
+    for k in range(steps):
+        for s in wl.stages:
+            s.fn(k % wl.copies)
+    torch.cuda.synchronize()
+
+
+def stage_breakdown(stages, stage_ms):
+    out = {}
+    for s, ms in zip(stages, stage_ms):
+        d = {"us": round(ms * 1e3, 2)}
+        if s.bytes:
+            d["GB/s"] = round(s.bytes / (ms * 1e-3) / 1e9, 1)
+            d["hbm_frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
+        if s.flops_alg:
+            d["TFLOP/s_alg"] = round(s.flops_alg / (ms * 1e-3) / 1e12, 1)
+            d["TFLOP/s_exec"] = round(s.flops_exec / (ms * 1e-3) / 1e12, 1)
+            d["mfma_frac_alg"] = round(d["TFLOP/s_alg"] / s.peak, 4)
+        out[s.name] = d
+    return out
+
+
+def roofline_of(stage, ms):
+    """Roofline object of a stage from its duration (algorithmic work / time)."""
+    if stage.kind == "mfma":
+        ach = stage.flops_alg / (ms * 1e-3) / 1e12
+        return {"kernel": stage.name, "bound": "mfma", "achieved": round(ach, 1), "peak": stage.peak,
+                "unit": "TFLOP/s", "frac": round(ach / stage.peak, 4), "us_per_launch": round(ms * 1e3, 2)}
+    ach = stage.bytes / (ms * 1e-3) / 1e9
+    return {"kernel": stage.name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "us_per_launch": round(ms * 1e3, 2)}
+
+
+# ---------------------------------------------------------------------------
+# Traffic records, calibration, context measurements
+# ---------------------------------------------------------------------------
 
 KERNEL_SOURCES = {"gemm": ["gemm.hip"], "prepare": ["prepare.hip"], "silu": ["glue.hip", "silu.h"],
                   "grouped": ["gemm.hip"], "compact": ["compact.hip"], "nvfp4": ["nvfp4.hip"]}
@@ -365,28 +521,6 @@ def copy_calibration(n_bytes, steps):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": n_bytes, "steps": steps}), flush=True)
-
-
-def cpu_baseline(oracle_sample, tokens_full, budget_s=20.0):
-    """Time the CPU oracle on a bounded row sample; grow the sample until it takes
-    a few seconds, stop before the budget."""
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max([i.get("num_threads", 1) for i in blas] or [1])
-        blas_name = blas[0].get("internal_api", "?") if blas else "?"
-    except Exception:
-        threads, blas_name = os.cpu_count() or 1, "?"
-    rows, spent = 4, 0.0
-    while True:
-        dt = oracle_sample(rows)
-        spent += dt
-        if dt > budget_s / 4 or rows * 2 > tokens_full or spent + 2.5 * dt > budget_s:
-            break
-        rows *= 2
-    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} of {tokens_full} tokens through the numpy/fp64 oracle of the same chain "
-                      f"(weights quantised inside the timed call), {dt:.2f} s; BLAS {blas_name} with {threads} threads"}
 
 
 def copy_rate(torch, n_bytes=1 << 30, reps=10):
@@ -437,29 +571,155 @@ def mfma_sustained_rate(torch, reps=5, unit="fp4"):
     return round(flops / (float(np.median(ts)) * 1e-3) / 1e12, 1)
 
 
-def cold_cache_times(stages, steps, torch):
+def cold_cache_times(torch, wl, steps):
     """Per-stage times with the caches cold: before each step a read of a
     1 GiB buffer evicts L2 and the 256 MB MALL, so every stage reads its
-    inputs from HBM (the timed loop runs steps back to back, where weights and
-    activations that fit stay cached between steps). The sweep reads rather
-    than writes: a write would leave the caches full of dirty lines whose
-    write-back would then be charged to the first stages. Returns (ms per
-    step, {stage: median us})."""
+    inputs from HBM. The sweep reads rather than writes: a write would leave
+    the caches full of dirty lines whose write-back would then be charged to
+    the first stages. Returns (ms per step, {stage: median us})."""
     scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    n = len(stages)
+    n = len(wl.stages)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
     for k in range(steps):
         scratch.amax()
         events[k][0].record()
-        for i, s in enumerate(stages):
-            s.fn()
+        for i, s in enumerate(wl.stages):
+            s.fn(k % wl.copies)
             events[k][i + 1].record()
     torch.cuda.synchronize()
     step_ms = float(np.median([events[k][0].elapsed_time(events[k][n]) for k in range(steps)]))
-    us = {s.name: round(1e3 * float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(steps)])), 2)
-          for i, s in enumerate(stages)}
+    us = {s.name: round(1e3 * float(np.median([events[k][i].elapsed_time(events[k][i + 1])
+                                               for k in range(steps)])), 2)
+          for i, s in enumerate(wl.stages)}
     del scratch
     return step_ms, us
+
+
+def run_config(torch, sq, name, steps, warmup):
+    """One of the other workloads, timed as the headline: whole-step graph
+    replays (weight copies rotated where the workload has several) for
+    tokens/s, per-stage back-to-back graphs for the stage times and the
+    roofline of the dominant stage."""
+    wl = build_workload(name, torch, sq)
+    warm(torch, wl, warmup)
+    graphs = capture_step_graphs(torch, wl)
+    time_step_graphs(torch, graphs, max(2, warmup))
+    settle(torch, graphs, 0.2)
+    ms_step, ev_step = time_step_graphs(torch, graphs, steps)
+    del graphs
+    stage_ms = time_stages_back_to_back(torch, wl)
+    dom = int(np.argmax(stage_ms))
+    out = {"workload": wl.cfg["workload"], "tokens": wl.tokens,
+           "tokens_per_s": round(wl.tokens / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
+           "gpu_ms_per_step": round(ev_step, 4), "stages": stage_breakdown(wl.stages, stage_ms),
+           "roofline": roofline_of(wl.stages[dom], stage_ms[dom])}
+    if wl.copies > 1:
+        out["weight_copies_rotated"] = wl.copies
+    del wl
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (a child process that never touches the GPU)
+# ---------------------------------------------------------------------------
+
+def _quantize_rows(w):
+    from oracle import quantize_weight_ref
+    return quantize_weight_ref(w)
+
+
+def _oracle_weights(w, workers):
+    """quantize_weight_ref over row chunks in a process pool (the oracle is
+    row-independent; this only spreads the one-off set-up over the cores)."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    chunks = np.array_split(w, max(1, workers * 2))
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork")) as ex:
+        parts = list(ex.map(_quantize_rows, chunks))
+    return np.concatenate([c for c, _ in parts]), np.concatenate([s for _, s in parts])
+
+
+def cpu_baseline_child(workload):
+    """Times the NumPy/float64 oracle of the headline chain on the host:
+    prepare stages and fp64 GEMM stages separately, on two row samples, and
+    extrapolates linearly (a fixed cost per call, such as dequantising W, plus
+    a per-token cost) to the full batch. Weights are quantised by the oracle
+    beforehand, outside the timed calls. Prints one JSON object."""
+    from oracle import linear_ref, prepare_ref, silu_mul_ref
+    from synth import workload_llama8b_mlp
+    if workload != "llama8b_mlp":
+        print(json.dumps(None))
+        return
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(cores, user_api="blas")
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas_name = blas[0].get("internal_api", "?") if blas else "?"
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    except Exception:
+        blas_name, threads = "?", cores
+    wl = workload_llama8b_mlp()
+    T, I = wl["x"].shape[0], wl["inter"]
+    t0 = time.perf_counter()
+    wgc, wgs = _oracle_weights(wl["w_gu"], min(cores, 16))
+    wdc, wds = _oracle_weights(wl["w_down"], min(cores, 16))
+    setup_s = time.perf_counter() - t0
+
+    def run(rows):
+        t = {}
+        a = time.perf_counter()
+        p1 = prepare_ref(wl["x"][:rows], wl["gamma"], 2, 4, rms_eps=1e-5)
+        b = time.perf_counter()
+        gu, _ = linear_ref(p1["bb_codes"], p1["bb_scales"], p1["res_codes"], p1["res_scales"], wgc, wgs)
+        c = time.perf_counter()
+        h = silu_mul_ref(gu.astype(np.float32), I)
+        p2 = prepare_ref(h, None, 2, 4)
+        d = time.perf_counter()
+        linear_ref(p2["bb_codes"], p2["bb_scales"], p2["res_codes"], p2["res_scales"], wdc, wds)
+        e = time.perf_counter()
+        t["prepare"] = (b - a) + (d - c)
+        t["gemm"] = (c - b) + (e - d)
+        return t
+
+    r1, r2 = 64, 256
+    t1, t2 = run(r1), run(r2)
+    est = {}
+    for k in ("prepare", "gemm"):
+        per = max((t2[k] - t1[k]) / (r2 - r1), 0.0)
+        fixed = max(t1[k] - per * r1, 0.0)
+        est[k] = {"s_per_token": per, "fixed_s": fixed, "full_batch_s": fixed + per * T}
+    full = est["prepare"]["full_batch_s"] + est["gemm"]["full_batch_s"]
+    print(json.dumps({
+        "value": round(T / full, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": f"the numpy/float64 oracle of the whole chain (prepare with RMSNorm, gate|up GEMM, silu_mul, "
+                  f"prepare(h), down GEMM) on the first {r1} and first {r2} of {T} tokens, timed per stage kind; "
+                  f"value = {T} tokens over the linear extrapolation (fixed + per-token cost) of both to the "
+                  f"full batch; oracle weight quantisation done beforehand ({setup_s:.1f} s, not timed)",
+        "prepare_s_sample": [round(t1["prepare"], 3), round(t2["prepare"], 3)],
+        "gemm_s_sample": [round(t1["gemm"], 3), round(t2["gemm"], 3)],
+        "prepare_tokens_per_s": round(T / est["prepare"]["full_batch_s"], 2),
+        "gemm_tokens_per_s": round(T / est["gemm"]["full_batch_s"], 2),
+        "blas": {"library": blas_name, "threads": threads}}), flush=True)
+
+
+def cpu_baseline(workload, timeout_s=600):
+    """Runs cpu_baseline_child in a child process (it never initialises the GPU)."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", "--workload", workload]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout_s, cwd=ROOT)
+    except subprocess.TimeoutExpired:
+        return {"error": f"oracle timing exceeded {timeout_s} s"}
+    if r.returncode != 0:
+        return {"error": r.stderr.strip().splitlines()[-1] if r.stderr.strip() else f"exit {r.returncode}"}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+# ---------------------------------------------------------------------------
+
+def log(msg):
+    print(f"# {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -469,20 +729,30 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama8b_mlp", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' `configs` object")
+    ap.add_argument("--config-steps", type=int, default=20, help="timed steps per workload in `configs`")
     ap.add_argument("--unfused", action="store_true",
-                    help="llama8b_mlp: run gate|up, silu_mul and prepare(h) as three kernels")
+                    help="run gate|up, silu_mul and prepare(h) as three kernels")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed step replays before the timed region (clocks reach their sustained "
+                         "state)")
     ap.add_argument("--profile-stage", default=None,
-                    help="run only this stage in warmup and timing (per-kernel profiling; not a step)")
+                    help="run only this stage, eagerly, in warmup and timing (per-kernel profiling; not a step)")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache stage timing")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a device copy of this many bytes (reference for counter scaling)")
     ap.add_argument("--calib", choices=["fp4", "f16"], default=None,
                     help="only run the MFMA rate calibration kernel (reference for clock and MFMA-busy counters)")
+    ap.add_argument("--cpu-baseline-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.cpu_baseline_child:
+        cpu_baseline_child(args.workload)
+        return
 
     import torch
     import activation_sparsity_fp4_amd as sq
@@ -490,116 +760,91 @@ def main():
         raise SystemExit("bench.py needs the GPU")
     torch.cuda.init()
     if args.calib:
-        import torch
         print(json.dumps({"calib": args.calib, "TFLOP/s": mfma_sustained_rate(torch, unit=args.calib)}), flush=True)
         return
     if args.copy_bytes:
         copy_calibration(args.copy_bytes, args.steps)
         return
-    print(f"# building inputs for {args.workload}", file=sys.stderr, flush=True)
-    stages, tokens, cfg, oracle_sample = build_workload(args.workload, torch, sq, args.unfused)
+    log(f"building inputs for {args.workload}")
+    wl = build_workload(args.workload, torch, sq, args.unfused)
     torch.cuda.synchronize()
-    if args.profile_stage:
-        stages = [s for s in stages if s.name == args.profile_stage]
-        if not stages:
+    profiling = args.profile_stage is not None
+    if profiling:
+        wl.stages = [s for s in wl.stages if s.name == args.profile_stage]
+        if not wl.stages:
             raise SystemExit(f"no stage {args.profile_stage!r} in workload {args.workload}")
 
-    for _ in range(args.warmup):
-        for s in stages:
-            s.fn()
-    torch.cuda.synchronize()
+    warm(torch, wl, args.warmup)
+    eager_ms, eager_stage_ms = time_eager(torch, wl, args.steps)
+    log(f"warmup and eager pass done ({eager_ms:.4f} ms per step); timing {args.steps} steps")
 
-    # Stage breakdown (untimed): HIP events between all stages, medians over
-    # `steps` steps; it names the dominant stage.
-    n = len(stages)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        ev = events[k]
-        ev[0].record()
-        for i, s in enumerate(stages):
-            s.fn()
-            ev[i + 1].record()
-    torch.cuda.synchronize()
-    stage_ms = [float(np.median([events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)]))
-                for i in range(n)]
-    dom_i = int(np.argmax(stage_ms))
-    print(f"# warmup and breakdown done, timing {args.steps} steps", file=sys.stderr, flush=True)
-
-    # Timed region: K steps back to back; HIP events (on the launch stream)
-    # bracket only the dominant stage, whose live median duration feeds the
-    # roofline (events between every stage would add their own gaps to the
-    # step).
-    dom_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        for i, s in enumerate(stages):
-            if i == dom_i:
-                dom_ev[k][0].record()
-                s.fn()
-                dom_ev[k][1].record()
-            else:
-                s.fn()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    dom_ms = float(np.median([dom_ev[k][0].elapsed_time(dom_ev[k][1]) for k in range(args.steps)]))
-
-    ms_per_step = 1e3 * wall / args.steps
-    breakdown = {}
-    for s, ms in zip(stages, stage_ms):
-        d = {"us": round(ms * 1e3, 2)}
-        if s.bytes:
-            d["GB/s"] = round(s.bytes / (ms * 1e-3) / 1e9, 1)
-            d["hbm_frac"] = round(d["GB/s"] / HBM_PEAK_GBS, 4)
-        if s.flops_alg:
-            d["TFLOP/s_alg"] = round(s.flops_alg / (ms * 1e-3) / 1e12, 1)
-            d["TFLOP/s_exec"] = round(s.flops_exec / (ms * 1e-3) / 1e12, 1)
-            d["mfma_frac_alg"] = round(d["TFLOP/s_alg"] / s.peak, 4)
-        breakdown[s.name] = d
-
-    # dominant kernel: the stage with the largest median duration in the breakdown;
-    # achieved = its algorithmic work over its live median duration in the timed region
-    dom = stages[dom_i]
-    traffic = recorded_traffic(args.workload, dom.name)
-    if dom.kind == "mfma":
-        ach = dom.flops_alg / (dom_ms * 1e-3) / 1e12
-        roof = {"kernel": dom.name, "bound": "mfma", "achieved": round(ach, 1), "peak": dom.peak,
-                "unit": "TFLOP/s", "frac": round(ach / dom.peak, 4), "traffic": traffic,
-                "us_per_launch": round(dom_ms * 1e3, 2)}
+    if args.eager or profiling:
+        ms_per_step, stage_ms = time_eager(torch, wl, args.steps)
+        gpu_ms_per_step = None
+        timing = "eager launches, HIP events between the stages"
     else:
-        ach = dom.bytes / (dom_ms * 1e-3) / 1e9
-        roof = {"kernel": dom.name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "us_per_launch": round(dom_ms * 1e3, 2)}
-    if dom.kind == "mfma" and not args.profile_stage and not args.no_cold:
+        graphs = capture_step_graphs(torch, wl)
+        time_step_graphs(torch, graphs, max(2, args.warmup))
+        settle(torch, graphs, args.settle)
+        ms_per_step, gpu_ms_per_step = time_step_graphs(torch, graphs, args.steps)
+        del graphs
+        stage_ms = time_stages_back_to_back(torch, wl)
+        timing = (f"after {args.warmup} warm-up steps and {args.settle} s of untimed replays (sustained clocks), "
+                  "timed region: whole-step HIP graph replays (kernel nodes only), HIP events around the region; "
+                  "stage times: a graph of 10 back-to-back launches of each stage, HIP events around its replays")
+    log(f"timed region done ({ms_per_step:.4f} ms per step)")
+
+    dom_i = int(np.argmax(stage_ms))
+    dom = wl.stages[dom_i]
+    roof = roofline_of(dom, stage_ms[dom_i])
+    roof["traffic"] = recorded_traffic(args.workload, dom.name)
+    if roof["traffic"] is not None:
+        roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roof["algorithmic_bytes"] = round(dom.bytes)
+    if dom.kind == "mfma" and not profiling and not args.no_cold:
         # context: the MFMA rate this GPU sustains with random operands (power-limited clock), and the
         # kernel's executed (dense-masked) rate as a fraction of it
         sustained = mfma_sustained_rate(torch, unit="fp4" if dom.peak == FP4_PEAK_TFLOPS else "f16")
         roof["sustained_mfma_TFLOPs"] = sustained
-        roof["frac_exec_of_sustained"] = round(dom.flops_exec / (dom_ms * 1e-3) / 1e12 / sustained, 4)
-    if traffic is not None:
-        roof["traffic_unit"] = "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
-        roof["algorithmic_bytes"] = round(dom.bytes)
+        roof["frac_exec_of_sustained"] = round(dom.flops_exec / (stage_ms[dom_i] * 1e-3) / 1e12 / sustained, 4)
+        roof["frac_alg_of_sustained"] = round(dom.flops_alg / (stage_ms[dom_i] * 1e-3) / 1e12 / sustained, 4)
 
-    value = tokens * args.steps / wall
     line = {
         "metric": "SharQ linear tokens/s (prepare GB/s and FP4 GEMM TFLOP/s as fractions of MI355X peak)",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": cfg.get("format", "mxfp4"), "data": "synthetic", "config": cfg, "roofline": roof, "stages": breakdown,
+        "value": round(wl.tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.cfg.get("format", "mxfp4"), "data": "synthetic", "config": wl.cfg,
+        "timing": timing, "roofline": roof, "stages": stage_breakdown(wl.stages, stage_ms),
+        "stage_sum_us": round(1e3 * sum(stage_ms), 2),
+        "gpu_ms_per_step": None if gpu_ms_per_step is None else round(gpu_ms_per_step, 4),
+        "eager": {"ms_per_step": round(eager_ms, 4), "stages_us": {s.name: round(1e3 * t, 2) for s, t in
+                                                                    zip(wl.stages, eager_stage_ms)}},
     }
-    if not args.profile_stage and not args.no_cold:
+    if not profiling and not args.no_cold:
         line["hbm_copy_GBps"] = copy_rate(torch)
-        cold_ms, cold_us = cold_cache_times(stages, args.steps, torch)
-        line["cold_cache"] = {"ms_per_step": round(cold_ms, 4), "tokens_per_s": round(tokens / (cold_ms * 1e-3), 1),
-                              "stages_us": cold_us,
-                              "note": "L2 and MALL evicted by a 1 GiB read before each step; medians; not the timed region"}
-    if args.profile_stage:
+        cold_ms, cold_us = cold_cache_times(torch, wl, args.steps)
+        line["cold_cache"] = {"ms_per_step": round(cold_ms, 4),
+                              "tokens_per_s": round(wl.tokens / (cold_ms * 1e-3), 1), "stages_us": cold_us,
+                              "note": "L2 and MALL evicted by a 1 GiB read before each eager step; medians; "
+                                      "not the timed region"}
+    if profiling:
         line["profile_stage"] = args.profile_stage
         line["note"] = "only this stage was run; value and ms_per_step are not a full step"
-    if oracle_sample is not None and not args.no_cpu_baseline and not args.profile_stage:
-        print("# timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(oracle_sample, tokens)
+    del wl
+    torch.cuda.empty_cache()
+
+    if args.workload == "llama8b_mlp" and not profiling and not args.no_configs:
+        configs = {}
+        for key, name in CONFIG_SET:
+            log(f"config {key}: {name}")
+            configs[key] = run_config(torch, sq, name, args.config_steps, 3)
+        line["configs"] = configs
+        _DECODE_WEIGHTS.clear()
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline and not profiling and args.workload == "llama8b_mlp":
+        log("timing the CPU oracle in a child process")
+        line["cpu_baseline"] = cpu_baseline(args.workload)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -1054,11 +1054,9 @@ __global__ __launch_bounds__(256) void split_reduce_silu_prepare_kernel(const fl
   uint32_t hb[16];
 #pragma unroll
   for (int k = 0; k < 32; k += 2) {
-    const uint32_t lo = bf16_rne_bits(silu_times(gv[k], uv[k]));
-    const uint32_t hi = bf16_rne_bits(silu_times(gv[k + 1], uv[k + 1]));
-    hb[k / 2] = lo | (hi << 16);
-    hv[k] = __uint_as_float(lo << 16);
-    hv[k + 1] = __uint_as_float(hi << 16);
+    hb[k / 2] = bf16x2_rne(silu_times(gv[k], uv[k]), silu_times(gv[k + 1], uv[k + 1]));
+    hv[k] = bf16_lo(hb[k / 2]);
+    hv[k + 1] = bf16_hi(hb[k / 2]);
   }
   if (out.h) {
     uint4* dst = reinterpret_cast<uint4*>(out.h + t * out.I + 32 * (int64_t)b);

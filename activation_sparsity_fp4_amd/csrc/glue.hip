@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
   for (int k = 0; k < 4; ++k) {
     const float a = silu_times(gv[2 * k], uv[2 * k]);
     const float b = silu_times(gv[2 * k + 1], uv[2 * k + 1]);
-    out[k] = bf16_rne_bits(a) | (bf16_rne_bits(b) << 16);
+    out[k] = bf16x2_rne(a, b);
   }
   reinterpret_cast<uint4*>(h + (int64_t)t * I)[c] = make_uint4(out[0], out[1], out[2], out[3]);
 }
@@ -41,8 +41,8 @@ __device__ __forceinline__ void combine_store(float4 acc, int64_t t, uint32_t c,
                                               uint16_t* __restrict__ out_bf16) {
   if (out) reinterpret_cast<float4*>(out + t * H)[c] = acc;
   if (out_bf16) {
-    const uint32_t lo = bf16_rne_bits(acc.x) | (bf16_rne_bits(acc.y) << 16);
-    const uint32_t hi = bf16_rne_bits(acc.z) | (bf16_rne_bits(acc.w) << 16);
+    const uint32_t lo = bf16x2_rne(acc.x, acc.y);
+    const uint32_t hi = bf16x2_rne(acc.z, acc.w);
     reinterpret_cast<uint2*>(out_bf16 + t * H)[c] = make_uint2(lo, hi);
   }
 }

@@ -33,11 +33,7 @@ __device__ __forceinline__ BlockOfLane block_of_lane(uint32_t stages, uint32_t b
   return block_of_item(gid >> 6, gid & 63, stages, blocks_per_row, rows);
 }
 
-// bf16 bits of a float32 value, rounded to nearest, ties to even (finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t b = __float_as_uint(f);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
+
 
 __device__ __forceinline__ void load_block(const uint16_t* p, uint4 (&raw)[4]) {
   const uint4* src = reinterpret_cast<const uint4*>(p);

@@ -18,6 +18,15 @@ constexpr int kBlock = 32;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Two floats rounded to bf16 (nearest, ties to even) by one gfx950
+// v_cvt_pk_bf16_f32: the low half holds a, the high half b. Finite inputs
+// (fp32 denormals are kept, so they round like every other value).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // E8M0 byte (exponent + 127) of a block from the bit pattern of its largest
 // magnitude (sign bit clear): floor(log2(amax)) - 2, clamped below at -127.
 // For a normal amax with exponent field f this is f - 129 (byte f - 2); f < 2

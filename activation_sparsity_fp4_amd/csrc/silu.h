@@ -8,9 +8,9 @@
 
 namespace sharq {
 
+// bf16 bits of f, rounded to nearest even (the hardware converter).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
-  const uint32_t b = __float_as_uint(f);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // silu(g) * u without overflow: with h = exp(-|g| / 2) (in (0, 1]),

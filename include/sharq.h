@@ -122,7 +122,8 @@ SHARQ_API int sharq_prepare(const uint16_t* x, int64_t T, int64_t K, int64_t ldx
  * other in index order, then the block sums by a pairwise tree over blocks in
  * index order (adjacent pairs, level by level, padded with zero blocks to a
  * power of two); mean, eps, sqrt and reciprocal are correctly rounded float64
- * operations. Two kernels run: the row scales, then the prepare.
+ * operations. One kernel runs: x is read from HBM once and the scale r of a
+ * row is formed before its blocks are coded.
  *  eps        > 0 and finite.
  *  gamma      bf16 [K] or NULL, K entries read (as sharq_prepare).
  *  rms_scale  fp32 [T], written with r (required).

@@ -14,7 +14,7 @@ from __future__ import annotations
 from typing import NamedTuple, Optional
 
 from . import _lib
-from ._lib import SharqError, status_string  # noqa: F401
+from ._lib import SCRATCHFREE_MAX_BYTES, SharqError, status_string  # noqa: F401
 
 __all__ = [
     "Prepared",
@@ -22,6 +22,7 @@ __all__ = [
     "prepare",
     "quantize_mxfp4",
     "linear",
+    "linear_scratchfree",
     "linear_grouped",
     "linear_silu_prepare",
     "linear_silu_prepare_into",
@@ -249,6 +250,29 @@ def linear(prep: Prepared, w: MXFP4, out=None, split_k: bool = True):
                    prep.res_scales.data_ptr(), w.codes.data_ptr(), w.scales.data_ptr(), T, O, K,
                    out.data_ptr(), out.stride(0), _stream(out.device))
     _lib.check("sharq_linear", st)
+    return out
+
+
+def linear_scratchfree(prep: Prepared, w: MXFP4, out):
+    """linear() with any K split's partials in the library's static scratch
+    array instead of a workspace: nothing is allocated, so `out` (fp32
+    [T, O]) is required. Raises SharqError (SHARQ_ESCRATCH) when the split
+    plan needs more than SCRATCHFREE_MAX_BYTES. Calls that overlap in time on
+    one GPU share the array and race."""
+    torch = _torch()
+    _check_prepared(prep)
+    _need(w.codes, torch.uint8, "w.codes", 3)
+    _need(w.scales, torch.uint8, "w.scales", 3)
+    T, K = prep.bb_codes.shape[1], prep.K
+    O = w.codes.shape[1]
+    if w.K != K:
+        raise ValueError("weight K does not match the activation K")
+    _check_stage_major(w.codes, w.scales, O, K, "w")
+    _check_matrix(out, torch.float32, T, O, "out")
+    st = _lib.call("sharq_linear_scratchfree", prep.bb_codes.data_ptr(), prep.bb_scales.data_ptr(),
+                   prep.res_codes.data_ptr(), prep.res_scales.data_ptr(), w.codes.data_ptr(), w.scales.data_ptr(),
+                   T, O, K, out.data_ptr(), out.stride(0), _stream(out.device))
+    _lib.check("sharq_linear_scratchfree", st)
     return out
 
 

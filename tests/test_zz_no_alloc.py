@@ -76,8 +76,10 @@ def test_scratchfree_without_split_and_refusal(sq):
     y_sf = torch.empty((T, O), dtype=torch.float32, device="cuda")
     assert _call(_lib.call, "sharq_linear_scratchfree", p, w, T, O, K, y_sf) == _lib.SHARQ_OK
     y = sq.linear(p, w)
+    y_b = sq.linear_scratchfree(p, w, torch.empty((T, O), dtype=torch.float32, device="cuda"))  # the binding
     torch.cuda.synchronize()
     assert np.array_equal(to_np(y_sf).view(np.uint32), to_np(y).view(np.uint32))
+    assert np.array_equal(to_np(y_b).view(np.uint32), to_np(y).view(np.uint32))
     Tb, Ob, Kb = 320, 8192, 28672
     assert _lib.call("sharq_linear_workspace_bytes", Tb, Ob, Kb) > _lib.SCRATCHFREE_MAX_BYTES
     assert _lib.call("sharq_linear_scratchfree", 16, 16, 16, 16, 16, 16, Tb, Ob, Kb, 16, Ob,

@@ -613,6 +613,10 @@ def run_config(torch, sq, name, steps, warmup):
            "tokens_per_s": round(wl.tokens / (ms_step * 1e-3), 1), "ms_per_step": round(ms_step, 4),
            "gpu_ms_per_step": round(ev_step, 4), "stages": stage_breakdown(wl.stages, stage_ms),
            "roofline": roofline_of(wl.stages[dom], stage_ms[dom])}
+    traffic = recorded_traffic(name, wl.stages[dom].name)
+    if traffic is not None:
+        out["roofline"]["traffic"] = traffic
+        out["roofline"]["algorithmic_bytes"] = round(wl.stages[dom].bytes)
     if wl.copies > 1:
         out["weight_copies_rotated"] = wl.copies
     del wl
